@@ -1,0 +1,159 @@
+/*
+ * mla.h -- C ABI of the token-sparse MLA decode library (libmla.so, gfx950 / MI355X).
+ *
+ * What the library computes: Multi-head Latent Attention decode in absorbed form, where every query
+ * head of a row attends over one shared 512-dim latent per selected token and the value is that same
+ * latent (page "flops/flashmla-decode-fp8-fp4-kv", section "Arithmetic intensity"; page
+ * "flops/attn-mla-kernel-support-matrix", section "Workarounds"). Tokens live in a quantized, paged
+ * cache of per-token records and are picked by an indices tensor of shape (batch, seq_len_q, topk)
+ * whose negative entries are ignored (page "flops/flashmla-decode-fp8-fp4-kv", section "Workarounds";
+ * page "deepseek-ai/FlashMLA", section "Key technical details").
+ *
+ * Call sequence (page "deepseek-ai/FlashMLA", section "How to use it"): obtain the tile-scheduler
+ * metadata once with mla_get_metadata, then call mla_sparse_decode for every generation step.
+ *
+ * Conventions for every entry point:
+ *   - Pointers marked "device" are HIP device pointers; "host" pointers are ordinary host memory.
+ *   - Tensors are dense and row-major in the shapes given; R = batch * seq_len_q query rows.
+ *   - The caller allocates and owns every buffer. The library allocates nothing, keeps no state
+ *     between calls and may be called from several host threads.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t passed as void*; NULL = default
+ *     stream). Device-side results are valid once the stream reaches that point.
+ *   - Errors are returned as negative mla_status codes; nothing throws across the ABI. Argument
+ *     checks happen on the host before anything is enqueued, so a failed call enqueues nothing.
+ *     A fault inside a kernel (for example an out-of-pool index) surfaces at the caller's next
+ *     synchronisation of the stream.
+ */
+#ifndef MLA_H_
+#define MLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MLA_HEAD_DIM 512          /* latent dim = d_qk = d_v */
+#define MLA_FP8_RECORD_BYTES 528  /* 512 e4m3 values, then 16 e8m0 scales (one per 32 values) */
+#define MLA_FP4_RECORD_BYTES 288  /* 256 bytes of e2m1 (even index in the low nibble), then 32 e4m3
+                                     scales (one per 16 values) */
+#define MLA_TILE_TOKENS 64        /* token slots per scheduling unit */
+#define MLA_SCHED_FIELDS 8        /* int32 fields per part in the schedule */
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_INVALID_ARG = -1,   /* null pointer, bad shape, misaligned buffer, inconsistent arguments */
+  MLA_ERR_UNSUPPORTED = -2,   /* shape outside what the kernels implement (e.g. head_dim != 512) */
+  MLA_ERR_WORKSPACE = -3,     /* workspace missing or smaller than mla_workspace_bytes() */
+  MLA_ERR_INDEX_RANGE = -4,   /* reserved for index range failures reported by helpers */
+  MLA_ERR_HIP = -5            /* a HIP runtime call or kernel launch failed */
+} mla_status;
+
+/* Human-readable text for a status code (static storage, never NULL). */
+const char* mla_error_string(int code);
+
+/*
+ * Number of parts the schedule will use, computed on the host (no device work).
+ * The metadata partitions the units of all rows over parts: a row owns ceil(topk/64) fp8 units then
+ * ceil(extra_topk/64) fp4 units (at least one unit in all); U = R * units_per_row; the part count is
+ * P_eff = max(1, min(num_parts, U / min_tiles_per_part)). num_parts == 0 selects the library's
+ * default for the current device and h_q. Returns MLA_OK and writes *num_parts_used (host).
+ * The pages call for "tile-scheduler metadata computed once before the decode loop" and "split
+ * decoding with num_splits" (page "flops/flashmla-decode-fp8-fp4-kv", section "Workarounds"); the
+ * partition rule itself is this library's own specification.
+ */
+int mla_metadata_parts(int batch, int seq_len_q, int h_q, int topk, int extra_topk, int num_parts,
+                       int min_tiles_per_part, int* num_parts_used);
+
+/*
+ * Compute the tile-scheduler metadata on the device (one small kernel on `stream`).
+ *   sched      device int32 [num_parts_used][8]: part p covers the contiguous units
+ *              [floor(p*U/P_eff), floor((p+1)*U/P_eff)) and stores
+ *              {begin_row, begin_tile, end_row, end_tile (exclusive end unit), first_slot, 0, 0, 0}
+ *              where first_slot is the workspace slot of its split of begin_row.
+ *   split_ptr  device int32 [R+1]: exclusive prefix sum of num_splits[r], the number of parts
+ *              meeting row r; row r's splits use workspace slots split_ptr[r] .. split_ptr[r+1]-1.
+ *   sched_capacity  number of [8]-int32 entries `sched` can hold (must be >= P_eff).
+ *   num_parts_used  host out: P_eff.
+ * The result depends only on the integer arguments, never on index values, so it is computed once
+ * per decode loop and reused for every step.
+ */
+int mla_get_metadata(int batch, int seq_len_q, int h_q, int topk, int extra_topk, int num_parts,
+                     int min_tiles_per_part, int32_t* sched, int sched_capacity, int32_t* split_ptr,
+                     int* num_parts_used, void* stream);
+
+/*
+ * Bytes of workspace mla_sparse_decode needs for this schedule: 0 when every part starts on a row
+ * boundary (no row is split, the workspace may be NULL); otherwise room for fp32 partial outputs
+ * [R + P_eff - 1][h_q][512] followed by fp32 partial lse [R + P_eff - 1][h_q], each 256-byte
+ * aligned. Host-only; returns 0 for invalid arguments as well.
+ */
+size_t mla_workspace_bytes(int batch, int seq_len_q, int h_q, int topk, int extra_topk,
+                           int num_parts_used);
+
+/*
+ * Sparse MLA decode: out, lse = attention of every query head over the selected tokens.
+ *   q              device bf16 [batch][seq_len_q][h_q][512]; 16-byte aligned.
+ *   k_cache        device uint8 [k_tokens][528] fp8 records (a paged pool viewed as flat tokens:
+ *                  token id = physical_block * block_size + offset); 16-byte aligned.
+ *   indices        device int32 [batch][seq_len_q][topk]: flat token ids into k_cache; entries < 0
+ *                  are ignored; entries >= k_tokens are a precondition violation (not checked on
+ *                  this path; see mla_validate_indices).
+ *   extra_k_cache  NULL, or device uint8 [extra_tokens][288] fp4 records, used next to the fp8
+ *                  k_cache (page "flops/flashmla-decode-fp8-fp4-kv", section "Arithmetic
+ *                  intensity"); 16-byte aligned.
+ *   extra_indices  NULL, or device int32 [batch][seq_len_q][extra_topk] into extra_k_cache.
+ *                  Each row attends with ONE softmax over the union of both selections.
+ *   softmax_scale  multiplier of q.k before the softmax (e.g. 1/sqrt(512)).
+ *   sched, split_ptr, num_parts_used  the metadata from mla_get_metadata for the same
+ *                  (batch, seq_len_q, h_q, topk, extra_topk).
+ *   workspace      device buffer, 256-byte aligned, of workspace_bytes >= mla_workspace_bytes(...)
+ *                  (NULL allowed when that is 0).
+ *   out            device bf16 [batch][seq_len_q][h_q][512]; 8-byte aligned.
+ *   lse            device fp32 [batch][seq_len_q][h_q]: natural-log log-sum-exp of the scaled scores
+ *                  (page "deepseek-ai/FlashMLA", section "How to use it", output and lse).
+ * A row with no valid entry gets out = 0 and lse = -inf. Rows split over several parts are merged
+ * by log-sum-exp in a second kernel on the same stream.
+ */
+int mla_sparse_decode(const void* q, const uint8_t* k_cache, int64_t k_tokens,
+                      const int32_t* indices, int topk, const uint8_t* extra_k_cache,
+                      int64_t extra_tokens, const int32_t* extra_indices, int extra_topk, int batch,
+                      int seq_len_q, int h_q, float softmax_scale, const int32_t* sched,
+                      const int32_t* split_ptr, int num_parts_used, void* workspace,
+                      size_t workspace_bytes, void* out, float* lse, void* stream);
+
+/*
+ * Log-sum-exp merge of split partials (the second half of split decoding, page
+ * "flops/flashmla-decode-fp8-fp4-kv", section "Workarounds"):
+ *   partial      device fp32 [S][h_q][512]: each split's output, already normalised by its own sum.
+ *   partial_lse  device fp32 [S][h_q]: each split's natural-log lse (-inf for an empty split).
+ *   split_ptr    device int32 [rows+1]: row r merges slots split_ptr[r] .. split_ptr[r+1]-1.
+ *   out          device bf16 [rows][h_q][512]; lse device fp32 [rows][h_q].
+ * For each (row, head): M = max lse_i, w_i = exp(lse_i - M), lse = M + log(sum w_i),
+ * out = sum w_i o_i / sum w_i; a row whose splits are all empty gets out = 0, lse = -inf.
+ */
+int mla_combine(const float* partial, const float* partial_lse, const int32_t* split_ptr, int rows,
+                int h_q, void* out, float* lse, void* stream);
+
+/*
+ * Diagnostic: dequantize whole records with the same device routine the decode kernel uses.
+ *   cache         device uint8 records of record_bytes (528 = fp8, 288 = fp4); 16-byte aligned.
+ *   idx           device int32 [n] token ids (all must be >= 0 and inside the cache).
+ *   out_bf16      device bf16 [n][512].
+ */
+int mla_dequant_records(const uint8_t* cache, int record_bytes, const int32_t* idx, int n,
+                        void* out_bf16, void* stream);
+
+/*
+ * Debug helper: count the entries of idx[0..n) that are >= num_tokens (negative entries are
+ * "ignored" entries and are not counted). Writes the count to *bad_count (device int32).
+ */
+int mla_validate_indices(const int32_t* idx, int64_t n, int64_t num_tokens, int32_t* bad_count,
+                         void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H_ */

@@ -1,0 +1,218 @@
+// C-ABI entry points of libmla (declared in include/mla.h): argument checks, the host side of the
+// schedule (part count, whether any row is split) and kernel launches. No allocation, no state.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/mla.h"
+#include "mla_internal.h"
+
+namespace {
+
+constexpr int kMaxRows = 1 << 24;
+
+int tiles_per_row(int topk, int extra_topk, int* tiles_k) {
+  const int tk = (topk + MLA_TILE_TOKENS - 1) / MLA_TILE_TOKENS;
+  const int tx = (extra_topk + MLA_TILE_TOKENS - 1) / MLA_TILE_TOKENS;
+  if (tiles_k) *tiles_k = tk;
+  return tk + tx > 0 ? tk + tx : 1;
+}
+
+// Waves per workgroup: one wave per 16 heads of the head group (32, 64 or 128 heads).
+int waves_for(int h_q) { return h_q <= 32 ? 2 : (h_q <= 64 ? 4 : 8); }
+int head_groups(int h_q) { return (h_q + 16 * waves_for(h_q) - 1) / (16 * waves_for(h_q)); }
+
+int default_parts(int h_q) {
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+      cus = v;
+  }
+  // workgroups resident per CU: 8-wave groups fill a CU (two waves per SIMD); smaller groups fit
+  // twice (limited by LDS, about 70-75 KB each)
+  const int per_cu = waves_for(h_q) == 8 ? 1 : 2;
+  const int parts = cus * per_cu / head_groups(h_q);
+  return parts > 0 ? parts : 1;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int check_shape(int batch, int seq_len_q, int h_q, int topk, int extra_topk) {
+  if (batch < 0 || seq_len_q < 0 || h_q <= 0 || topk < 0 || extra_topk < 0) return MLA_ERR_INVALID_ARG;
+  if ((int64_t)batch * seq_len_q > kMaxRows) return MLA_ERR_UNSUPPORTED;
+  if (h_q > 4096) return MLA_ERR_UNSUPPORTED;
+  if (topk > (1 << 28) || extra_topk > (1 << 28)) return MLA_ERR_UNSUPPORTED;
+  return MLA_OK;
+}
+
+int resolve_parts(int batch, int seq_len_q, int h_q, int topk, int extra_topk, int num_parts,
+                  int min_tiles_per_part, int* out) {
+  int rc = check_shape(batch, seq_len_q, h_q, topk, extra_topk);
+  if (rc != MLA_OK) return rc;
+  if (num_parts < 0 || min_tiles_per_part < 1 || !out) return MLA_ERR_INVALID_ARG;
+  if (num_parts == 0) num_parts = default_parts(h_q);
+  const int64_t units = (int64_t)batch * seq_len_q * tiles_per_row(topk, extra_topk, nullptr);
+  int64_t p = units / min_tiles_per_part;
+  if (p > num_parts) p = num_parts;
+  if (p < 1) p = 1;
+  if (p > (1 << 20)) return MLA_ERR_UNSUPPORTED;
+  *out = (int)p;
+  return MLA_OK;
+}
+
+// True when some part boundary falls strictly inside a row (then that row has several splits).
+bool any_split(int64_t rows, int tiles, int parts) {
+  const int64_t units = rows * tiles;
+  for (int64_t p = 1; p < parts; ++p)
+    if (((p * units) / parts) % tiles != 0) return true;
+  return false;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_error_string(int code) {
+  switch (code) {
+    case MLA_OK: return "success";
+    case MLA_ERR_INVALID_ARG: return "invalid argument (null pointer, shape, alignment or consistency)";
+    case MLA_ERR_UNSUPPORTED: return "unsupported shape";
+    case MLA_ERR_WORKSPACE: return "workspace missing or too small";
+    case MLA_ERR_INDEX_RANGE: return "index outside the cache";
+    case MLA_ERR_HIP: return "HIP runtime or kernel launch failure";
+    default: return "unknown mla status";
+  }
+}
+
+int mla_metadata_parts(int batch, int seq_len_q, int h_q, int topk, int extra_topk, int num_parts,
+                       int min_tiles_per_part, int* num_parts_used) {
+  return resolve_parts(batch, seq_len_q, h_q, topk, extra_topk, num_parts, min_tiles_per_part,
+                       num_parts_used);
+}
+
+int mla_get_metadata(int batch, int seq_len_q, int h_q, int topk, int extra_topk, int num_parts,
+                     int min_tiles_per_part, int32_t* sched, int sched_capacity, int32_t* split_ptr,
+                     int* num_parts_used, void* stream) {
+  int parts = 0;
+  int rc = resolve_parts(batch, seq_len_q, h_q, topk, extra_topk, num_parts, min_tiles_per_part,
+                         &parts);
+  if (rc != MLA_OK) return rc;
+  if (!sched || !split_ptr || sched_capacity < parts) return MLA_ERR_INVALID_ARG;
+  const int rows = batch * seq_len_q;
+  const int tiles = tiles_per_row(topk, extra_topk, nullptr);
+  if (mla::launch_metadata(rows, tiles, parts, sched, split_ptr, (hipStream_t)stream) != 0)
+    return MLA_ERR_HIP;
+  *num_parts_used = parts;
+  return MLA_OK;
+}
+
+static size_t split_workspace_bytes(int batch, int seq_len_q, int h_q, int num_parts_used) {
+  const size_t slots = (size_t)batch * seq_len_q + (size_t)num_parts_used - 1;
+  return align256(slots * h_q * MLA_HEAD_DIM * sizeof(float)) + align256(slots * h_q * sizeof(float));
+}
+
+size_t mla_workspace_bytes(int batch, int seq_len_q, int h_q, int topk, int extra_topk,
+                           int num_parts_used) {
+  if (check_shape(batch, seq_len_q, h_q, topk, extra_topk) != MLA_OK || num_parts_used < 1) return 0;
+  const int64_t rows = (int64_t)batch * seq_len_q;
+  if (rows == 0 || !any_split(rows, tiles_per_row(topk, extra_topk, nullptr), num_parts_used)) return 0;
+  return split_workspace_bytes(batch, seq_len_q, h_q, num_parts_used);
+}
+
+int mla_sparse_decode(const void* q, const uint8_t* k_cache, int64_t k_tokens,
+                      const int32_t* indices, int topk, const uint8_t* extra_k_cache,
+                      int64_t extra_tokens, const int32_t* extra_indices, int extra_topk, int batch,
+                      int seq_len_q, int h_q, float softmax_scale, const int32_t* sched,
+                      const int32_t* split_ptr, int num_parts_used, void* workspace,
+                      size_t workspace_bytes, void* out, float* lse, void* stream) {
+  int rc = check_shape(batch, seq_len_q, h_q, topk, extra_topk);
+  if (rc != MLA_OK) return rc;
+  const int rows = batch * seq_len_q;
+  if (rows == 0) return MLA_OK;
+  if (!q || !out || !lse || !sched || !split_ptr || num_parts_used < 1) return MLA_ERR_INVALID_ARG;
+  if (topk > 0 && (!k_cache || !indices || k_tokens <= 0)) return MLA_ERR_INVALID_ARG;
+  if (extra_topk > 0 && (!extra_k_cache || !extra_indices || extra_tokens <= 0))
+    return MLA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(out, 8) || !aligned(lse, 4) || !aligned(k_cache, 16) ||
+      !aligned(extra_k_cache, 16) || !aligned(indices, 4) || !aligned(extra_indices, 4))
+    return MLA_ERR_INVALID_ARG;
+  if (!std::isfinite(softmax_scale)) return MLA_ERR_INVALID_ARG;
+  int tiles_k = 0;
+  const int tiles = tiles_per_row(topk, extra_topk, &tiles_k);
+  const bool split = any_split(rows, tiles, num_parts_used);
+  float* part_o = nullptr;
+  float* part_lse = nullptr;
+  if (split) {
+    const size_t need = split_workspace_bytes(batch, seq_len_q, h_q, num_parts_used);
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return MLA_ERR_WORKSPACE;
+    const size_t slots = (size_t)rows + (size_t)num_parts_used - 1;
+    part_o = static_cast<float*>(workspace);
+    part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                        align256(slots * h_q * MLA_HEAD_DIM * sizeof(float)));
+  }
+  mla::DecodeParams p;
+  p.q = static_cast<const uint16_t*>(q);
+  p.kc = k_cache;
+  p.idx = indices;
+  p.xc = extra_topk > 0 ? extra_k_cache : nullptr;
+  p.xidx = extra_topk > 0 ? extra_indices : nullptr;
+  p.topk = topk;
+  p.extra_topk = extra_topk;
+  p.tiles_k = tiles_k;
+  p.tiles = tiles;
+  p.rows = rows;
+  p.h_q = h_q;
+  p.scale_log2 = softmax_scale * 1.4426950408889634f;
+  p.sched = sched;
+  p.split_ptr = split_ptr;
+  p.part_o = part_o;
+  p.part_lse = part_lse;
+  p.out = static_cast<uint16_t*>(out);
+  p.lse = lse;
+  hipStream_t s = (hipStream_t)stream;
+  if (mla::launch_sparse_decode(p, num_parts_used, head_groups(h_q), waves_for(h_q), s) != 0)
+    return MLA_ERR_HIP;
+  if (split && mla::launch_combine(part_o, part_lse, split_ptr, rows, h_q, p.out, lse, true, s) != 0)
+    return MLA_ERR_HIP;
+  return MLA_OK;
+}
+
+int mla_combine(const float* partial, const float* partial_lse, const int32_t* split_ptr, int rows,
+                int h_q, void* out, float* lse, void* stream) {
+  if (rows < 0 || h_q <= 0 || h_q > 65535) return MLA_ERR_INVALID_ARG;
+  if (rows == 0) return MLA_OK;
+  if (!partial || !partial_lse || !split_ptr || !out || !lse) return MLA_ERR_INVALID_ARG;
+  if (!aligned(partial, 16) || !aligned(out, 8)) return MLA_ERR_INVALID_ARG;
+  if (rows > kMaxRows) return MLA_ERR_UNSUPPORTED;
+  return mla::launch_combine(partial, partial_lse, split_ptr, rows, h_q,
+                             static_cast<uint16_t*>(out), lse, false, (hipStream_t)stream) == 0
+             ? MLA_OK
+             : MLA_ERR_HIP;
+}
+
+int mla_dequant_records(const uint8_t* cache, int record_bytes, const int32_t* idx, int n,
+                        void* out_bf16, void* stream) {
+  if (n < 0) return MLA_ERR_INVALID_ARG;
+  if (record_bytes != MLA_FP8_RECORD_BYTES && record_bytes != MLA_FP4_RECORD_BYTES)
+    return MLA_ERR_UNSUPPORTED;
+  if (n == 0) return MLA_OK;
+  if (!cache || !idx || !out_bf16 || !aligned(cache, 16) || !aligned(out_bf16, 16))
+    return MLA_ERR_INVALID_ARG;
+  return mla::launch_dequant(cache, record_bytes, idx, n, static_cast<uint16_t*>(out_bf16),
+                             (hipStream_t)stream) == 0
+             ? MLA_OK
+             : MLA_ERR_HIP;
+}
+
+int mla_validate_indices(const int32_t* idx, int64_t n, int64_t num_tokens, int32_t* bad_count,
+                         void* stream) {
+  if (n < 0 || num_tokens < 0 || !bad_count || (n > 0 && !idx)) return MLA_ERR_INVALID_ARG;
+  return mla::launch_validate(idx, n, num_tokens, bad_count, (hipStream_t)stream) == 0 ? MLA_OK
+                                                                                       : MLA_ERR_HIP;
+}
+
+}  // extern "C"

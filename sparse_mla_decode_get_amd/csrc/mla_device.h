@@ -1,0 +1,92 @@
+// Device-side building blocks shared by the gfx950 kernels of libmla: vector types, the in-register
+// dequantisation of record chunks, and a few wave-level helpers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kHeadDim = 512;
+constexpr int kFp8Rec = 528;      // 512 e4m3 + 16 e8m0
+constexpr int kFp4Rec = 288;      // 256 packed e2m1 + 32 e4m3
+constexpr int kFp8Chunks = 33;    // 16-byte chunks per fp8 record (32 data + 1 scale chunk)
+constexpr int kFp4Chunks = 18;    // 16 data chunks + 2 scale chunks
+constexpr int kUnitTokens = 64;   // scheduling unit
+constexpr int kSubTokens = 32;    // kernel tile: tokens per sub-tile
+
+__device__ __forceinline__ bf16x8 cat4(bf16x2 a, bf16x2 b, bf16x2 c, bf16x2 d) {
+  bf16x4 ab = __builtin_shufflevector(a, b, 0, 1, 2, 3);
+  bf16x4 cd = __builtin_shufflevector(c, d, 0, 1, 2, 3);
+  return __builtin_shufflevector(ab, cd, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// fp8 chunk -> bf16. `raw` holds 16 consecutive e4m3 values of one record (little-endian byte
+// order: element i in byte i); `scale_byte` is the e8m0 scale shared by them. gfx950's scaled
+// convert reads only the exponent field of its f32 scale operand and applies it as 2^(e - 127), so
+// placing the e8m0 byte in that field gives exactly x * 2^(byte - 127) rounded once to bf16
+// (exact whenever the product is representable, NaN for the e8m0 NaN byte 0xFF).
+__device__ __forceinline__ void dequant_fp8_16(u32x4 raw, uint32_t scale_byte, bf16x8& lo,
+                                               bf16x8& hi) {
+  const float s = __builtin_bit_cast(float, scale_byte << 23);
+  bf16x2 a0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[0], s, false);
+  bf16x2 a1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[0], s, true);
+  bf16x2 a2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[1], s, false);
+  bf16x2 a3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[1], s, true);
+  bf16x2 b0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[2], s, false);
+  bf16x2 b1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[2], s, true);
+  bf16x2 b2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[3], s, false);
+  bf16x2 b3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[3], s, true);
+  lo = cat4(a0, a1, a2, a3);
+  hi = cat4(b0, b1, b2, b3);
+}
+
+// e4m3 byte (low 8 bits of `b`) -> f32, exact.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(b & 0xFFu, 1.0f, false)[0];
+}
+
+// Two e2m1 values of byte `B` of `w` -> bf16 pair times an e4m3 scale value. The scaled convert
+// only honours power-of-two scales, so the e4m3 scale is applied as an f32 multiply; e2m1 * e4m3
+// has at most 6 significant bits, so the product and its bf16 rounding are exact.
+template <int B>
+__device__ __forceinline__ bf16x2 fp4_byte(uint32_t w, float scale) {
+  f32x2 v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, B);
+  bf16x2 r;
+  r[0] = (__bf16)(v[0] * scale);
+  r[1] = (__bf16)(v[1] * scale);
+  return r;
+}
+
+// fp4 half-chunk -> bf16: `w0`,`w1` hold 8 bytes = 16 e2m1 values (element 2k in the low nibble of
+// byte k), all sharing the e4m3 scale value `scale`.
+__device__ __forceinline__ void dequant_fp4_16(uint32_t w0, uint32_t w1, float scale, bf16x8& lo,
+                                               bf16x8& hi) {
+  lo = cat4(fp4_byte<0>(w0, scale), fp4_byte<1>(w0, scale), fp4_byte<2>(w0, scale),
+            fp4_byte<3>(w0, scale));
+  hi = cat4(fp4_byte<0>(w1, scale), fp4_byte<1>(w1, scale), fp4_byte<2>(w1, scale),
+            fp4_byte<3>(w1, scale));
+}
+
+// Pairwise reduction with the lane 32 apart (lane l <-> l ^ 32) via v_permlane32_swap.
+__device__ __forceinline__ float max_xor32(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
+                                            __builtin_bit_cast(uint32_t, x), false, false);
+  return fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
+                                            __builtin_bit_cast(uint32_t, x), false, false);
+  return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
+}
+
+}  // namespace mla

@@ -1,0 +1,38 @@
+// Host/device interface between the C-ABI entry points (mla_api.cpp) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+struct DecodeParams {
+  const uint16_t* q;         // bf16 [rows][h_q][512]
+  const uint8_t* kc;         // fp8 records
+  const int32_t* idx;        // [rows][topk]
+  const uint8_t* xc;         // fp4 records (may be null when extra_topk == 0)
+  const int32_t* xidx;       // [rows][extra_topk]
+  int topk, extra_topk;
+  int tiles_k, tiles;        // fp8 units per row, all units per row
+  int rows, h_q;
+  float scale_log2;          // softmax_scale * log2(e)
+  const int32_t* sched;      // [parts][8]
+  const int32_t* split_ptr;  // [rows + 1]
+  float* part_o;             // workspace partial outputs [slots][h_q][512]
+  float* part_lse;           // workspace partial lse [slots][h_q]
+  uint16_t* out;             // bf16 [rows][h_q][512]
+  float* lse;                // [rows][h_q]
+};
+
+int launch_sparse_decode(const DecodeParams& p, int parts, int groups, int nw, hipStream_t stream);
+int launch_metadata(int rows, int tiles, int parts, int32_t* sched, int32_t* split_ptr,
+                    hipStream_t stream);
+int launch_combine(const float* partial, const float* partial_lse, const int32_t* split_ptr,
+                   int rows, int h_q, uint16_t* out, float* lse, bool skip_single,
+                   hipStream_t stream);
+int launch_dequant(const uint8_t* cache, int record_bytes, const int32_t* idx, int n,
+                   uint16_t* out, hipStream_t stream);
+int launch_validate(const int32_t* idx, int64_t n, int64_t num_tokens, int32_t* bad,
+                    hipStream_t stream);
+
+}  // namespace mla

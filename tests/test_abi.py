@@ -1,0 +1,94 @@
+"""C-ABI checks that need no GPU: the library loads, exports every declared entry point, and its
+host-side logic (part count, workspace size, argument errors) agrees with the oracle's partition."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import sparse_mla_decode_get_amd as mla
+from oracle import oracle_metadata, part_count, tiles_per_row
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "mla.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(mla.library_path()):
+        pytest.skip("libmla.so not built")
+    return mla.load_library()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared()
+    assert len(names) >= 8
+    raw = ctypes.CDLL(mla.library_path())
+    for n in names:
+        assert hasattr(raw, n), n
+
+
+def test_error_strings(lib):
+    for code in (0, -1, -2, -3, -4, -5, 7):
+        assert isinstance(mla.error_string(code), str) and mla.error_string(code)
+
+
+@pytest.mark.parametrize("batch,seq,topk,extra,parts,min_tiles",
+                         [(1, 1, 128, 0, 256, 1), (128, 2, 2048, 0, 256, 1), (32, 1, 2048, 0, 512, 1),
+                          (64, 1, 2048, 512, 512, 4), (8, 1, 131072, 0, 256, 1), (3, 2, 150, 70, 7, 2),
+                          (2, 1, 0, 0, 4, 1)])
+def test_part_count_and_workspace_match_oracle(lib, batch, seq, topk, extra, parts, min_tiles):
+    p = mla.metadata_parts(batch, seq, 64, topk, extra, parts, min_tiles)
+    assert p == part_count(batch * seq, tiles_per_row(topk, extra), parts, min_tiles)
+    _, split_ptr, p_oracle = oracle_metadata(batch, seq, topk, extra, parts, min_tiles) \
+        if batch * seq * tiles_per_row(topk, extra) <= 4096 else (None, None, p)
+    ws = mla.workspace_bytes(batch, seq, 64, topk, extra, p)
+    if split_ptr is not None:
+        split = bool(np.any(np.diff(split_ptr) > 1))
+        assert (ws > 0) == split
+        if split:
+            slots = batch * seq + p - 1
+            assert ws >= slots * 64 * 512 * 4 + slots * 64 * 4
+
+
+def test_headline_schedule_needs_no_workspace(lib):
+    p = mla.metadata_parts(128, 2, 128, 2048, 0, 256, 1)
+    assert p == 256 and mla.workspace_bytes(128, 2, 128, 2048, 0, p) == 0
+
+
+def test_argument_errors_before_any_device_work(lib):
+    L = lib
+    null = None
+    # decode with null pointers -> invalid argument (checked on the host, nothing enqueued)
+    rc = L.mla_sparse_decode(null, null, 0, null, 16, null, 0, null, 0, 1, 1, 16, 0.1, null, null, 1,
+                             null, 0, null, null, null)
+    assert rc == -1
+    rc = L.mla_sparse_decode(null, null, 0, null, -1, null, 0, null, 0, 1, 1, 16, 0.1, null, null, 1,
+                             null, 0, null, null, null)
+    assert rc == -1
+    assert L.mla_combine(null, null, null, 4, 16, null, null, null) == -1
+    assert L.mla_dequant_records(null, 100, null, 4, null, null) == -2
+    assert L.mla_validate_indices(null, 4, 10, null, null) == -1
+    out = ctypes.c_int(0)
+    assert L.mla_metadata_parts(1, 1, 16, 128, 0, 4, 0, ctypes.byref(out)) == -1   # min_tiles 0
+    assert L.mla_metadata_parts(-1, 1, 16, 128, 0, 4, 1, ctypes.byref(out)) == -1
+    assert L.mla_get_metadata(1, 1, 16, 128, 0, 4, 1, null, 4, null, ctypes.byref(out), null) == -1
+    # zero rows is a no-op
+    assert L.mla_sparse_decode(null, null, 0, null, 16, null, 0, null, 0, 0, 1, 16, 0.1, null, null,
+                               1, null, 0, null, null, null) == 0
+
+
+def test_resource_report_parser():
+    from sparse_mla_decode_get_amd.build import _parse_resources
+    text = ("x.hip:1:1: remark: Function Name: kern [-Rpass]\n"
+            "x.hip:1:1: remark:     VGPRs: 12 [-Rpass]\n"
+            "x.hip:1:1: remark:     ScratchSize [bytes/lane]: 0 [-Rpass]\n"
+            "x.hip:1:1: remark:     VGPRs Spill: 3 [-Rpass]\n")
+    r = _parse_resources(text)
+    assert r == {"kern": {"VGPRs": 12, "ScratchSize [bytes/lane]": 0, "VGPRs Spill": 3}}

@@ -1,0 +1,217 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 CPU oracle.
+
+Bit-exact: record dequantisation (in the exact bf16 range) and the tile-scheduler metadata.
+Within tolerance (max |d out| <= 2e-2 max |ref| per row, |d lse| <= 1e-3): decode and merge, on
+small shapes spanning several tiles with ragged tails and edge cases, and on sampled rows of the
+full-size workloads in the launch configuration the benchmark times.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import sparse_mla_decode_get_amd as mla
+from oracle import (E4M3, dequant_fp4_records, dequant_fp8_records, oracle_combine, oracle_decode,
+                    oracle_decode_rows, oracle_metadata, oracle_split_decode)
+from workloads import CONFIGS, Spec, make_workload
+from tests.gpu_helpers import bf16_rne, bf16_to_f64, check_rows, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _decode(w, num_parts=0, min_tiles=1):
+    d = to_dev(w)
+    b, s, h, _ = d["q"].shape
+    extra = d["extra_indices"].shape[2] if "extra_indices" in d else 0
+    md = mla.get_metadata(b, s, h, d["indices"].shape[2], extra, num_parts, min_tiles)
+    out, lse = mla.sparse_decode(d["q"], d["k_cache"], d["indices"], w["softmax_scale"], md,
+                                 d.get("extra_k_cache"), d.get("extra_indices"))
+    torch.cuda.synchronize()
+    return out, lse, md
+
+
+def _oracle(w):
+    return oracle_decode(w["q_bits"], w["k_cache"], w["indices"], w["softmax_scale"],
+                         w["extra_k_cache"], w["extra_indices"])
+
+
+# ----------------------------------------------------------------------------- dequant (bit-exact)
+
+def test_fp8_dequant_bit_exact_over_the_exact_scale_range():
+    recs = []
+    for b in range(3, 247):
+        r = np.empty(528, dtype=np.uint8)
+        r[:512] = np.tile(np.arange(256, dtype=np.uint8), 2)
+        r[512:] = b
+        recs.append(r)
+    recs = np.stack(recs)
+    idx = torch.arange(len(recs), dtype=torch.int32, device="cuda")
+    got = bf16_to_f64(mla.dequant_records(torch.from_numpy(recs).cuda(), 528, idx))
+    ref = dequant_fp8_records(recs)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])           # exact: no rounding in this range
+
+
+def test_fp8_dequant_edge_scales_round_to_nearest_and_nan():
+    recs = []
+    for b in (0, 1, 2, 247, 250, 254, 255):
+        r = np.empty(528, dtype=np.uint8)
+        r[:512] = np.tile(np.arange(256, dtype=np.uint8), 2)
+        r[512:] = b
+        recs.append(r)
+    recs = np.stack(recs)
+    idx = torch.arange(len(recs), dtype=torch.int32, device="cuda")
+    got = bf16_to_f64(mla.dequant_records(torch.from_numpy(recs).cuda(), 528, idx))
+    ref = bf16_rne(dequant_fp8_records(recs))
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+
+
+def test_fp4_dequant_bit_exact_all_codes_and_scales():
+    recs = []
+    for k in range(8):                                    # 8 records x 32 scales = all 256 e4m3 codes
+        r = np.empty(288, dtype=np.uint8)
+        r[:256] = np.arange(256, dtype=np.uint8)          # every (low, high) nibble pair
+        r[256:] = np.arange(32 * k, 32 * k + 32, dtype=np.uint8)
+        recs.append(r)
+    recs = np.stack(recs)
+    idx = torch.arange(len(recs), dtype=torch.int32, device="cuda")
+    got = bf16_to_f64(mla.dequant_records(torch.from_numpy(recs).cuda(), 288, idx))
+    ref = dequant_fp4_records(recs)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+
+
+def test_dequant_gathers_by_index():
+    rng = np.random.default_rng(0)
+    recs = rng.integers(0, 256, size=(64, 528), dtype=np.uint8)
+    recs[:, 512:] = rng.integers(100, 150, size=(64, 16))
+    recs[:, :512][recs[:, :512] & 0x7F == 0x7F] = 0      # no NaN codes
+    sel = np.array([5, 0, 63, 5, 17], dtype=np.int32)
+    got = bf16_to_f64(mla.dequant_records(torch.from_numpy(recs).cuda(), 528,
+                                          torch.from_numpy(sel).cuda()))
+    assert np.array_equal(got, dequant_fp8_records(recs[sel]))
+
+
+# ---------------------------------------------------------------------------- metadata (bit-exact)
+
+@pytest.mark.parametrize("batch,seq,topk,extra,parts,min_tiles", [
+    (1, 1, 128, 0, 256, 1), (128, 2, 2048, 0, 256, 1), (32, 1, 2048, 0, 512, 1),
+    (64, 1, 2048, 512, 512, 1), (8, 1, 131072, 0, 256, 1), (3, 2, 150, 70, 7, 2), (5, 1, 64, 0, 3, 1),
+    (2, 1, 0, 0, 4, 1), (1, 1, 2048, 0, 256, 1), (700, 3, 70, 0, 1000, 1), (1500, 1, 128, 0, 999, 3)])
+def test_metadata_bit_exact(batch, seq, topk, extra, parts, min_tiles):
+    md = mla.get_metadata(batch, seq, 64, topk, extra, parts, min_tiles)
+    torch.cuda.synchronize()
+    sched, split_ptr, p_eff = oracle_metadata(batch, seq, topk, extra, parts, min_tiles)
+    assert md.num_parts == p_eff
+    assert np.array_equal(md.sched.cpu().numpy(), sched)
+    assert np.array_equal(md.split_ptr.cpu().numpy(), split_ptr)
+
+
+# ----------------------------------------------------------------------------- decode (tolerance)
+
+SMALL = [
+    Spec("cfg0", 1, 1, 16, 128, 4096, neg="frac5"),
+    Spec("h32_ragged", 2, 1, 32, 300, 4096, neg="frac5"),
+    Spec("h64_sq2", 2, 2, 64, 257, 2048),
+    Spec("h128_spread", 2, 2, 128, 200, 4096, values="spread", neg="tail10"),
+    Spec("h128_topk1", 3, 1, 128, 1, 512),
+    Spec("h100_masked_heads", 2, 1, 100, 96, 1024),
+    Spec("h200_two_groups", 1, 2, 200, 130, 1024, neg="frac5"),
+    Spec("h1", 2, 1, 1, 64, 512),
+    Spec("all_ignored", 2, 1, 64, 100, 1024, neg="all"),
+    Spec("mixed_fp4", 2, 1, 64, 130, 2048, extra_topk=70, extra_tokens_per_seq=1024),
+    Spec("mixed_h128", 2, 2, 128, 64, 1024, extra_topk=200, extra_tokens_per_seq=1024,
+         values="spread"),
+    Spec("fp4_only_extra", 2, 1, 32, 0, 64, extra_topk=100, extra_tokens_per_seq=512),
+]
+
+
+@pytest.mark.parametrize("spec", SMALL, ids=[s.name for s in SMALL])
+def test_decode_small_default_schedule(spec):
+    w = make_workload(spec, seed=7)
+    out, lse, _ = _decode(w)
+    ref_out, ref_lse = _oracle(w)
+    check_rows(out, lse, ref_out, ref_lse, spec.name)
+
+
+@pytest.mark.parametrize("spec,parts,min_tiles", [
+    (Spec("split_h128", 2, 1, 128, 2048, 8192), 7, 1),
+    (Spec("split_h64", 3, 2, 64, 700, 4096, neg="tail10"), 5, 1),
+    (Spec("split_mixed", 2, 1, 64, 300, 2048, extra_topk=150, extra_tokens_per_seq=1024), 9, 1),
+    (Spec("split_h16", 1, 1, 16, 1000, 4096, neg="frac5"), 16, 1),
+    (Spec("one_part", 3, 2, 128, 150, 2048), 1, 1),
+    (Spec("split_empty_rows", 2, 1, 64, 500, 2048, neg="all"), 4, 1),
+], ids=lambda x: x.name if isinstance(x, Spec) else str(x))
+def test_decode_split_rows(spec, parts, min_tiles):
+    w = make_workload(spec, seed=11)
+    out, lse, md = _decode(w, num_parts=parts, min_tiles=min_tiles)
+    if spec.name != "one_part":
+        assert md.workspace is not None            # some row really is split
+    ref_out, ref_lse = _oracle(w)
+    check_rows(out, lse, ref_out, ref_lse, spec.name)
+
+
+def test_split_and_unsplit_agree_on_gpu():
+    w = make_workload(Spec("agree", 2, 2, 128, 1024, 8192, values="spread"), seed=5)
+    o1, l1, _ = _decode(w, num_parts=4)            # one part per row
+    o2, l2, md = _decode(w, num_parts=13)          # rows split
+    assert md.workspace is not None
+    ref_out, ref_lse = _oracle(w)
+    check_rows(o1, l1, ref_out, ref_lse, "unsplit")
+    check_rows(o2, l2, ref_out, ref_lse, "split")
+
+
+def test_combine_matches_oracle_merge():
+    spec = Spec("comb", 3, 1, 32, 600, 4096, neg="tail10")
+    w = make_workload(spec, seed=3)
+    sched, split_ptr, _ = oracle_metadata(3, 1, 600, 0, 7, 1)
+    po, pl = oracle_split_decode(w["q_bits"], w["k_cache"], w["indices"], w["softmax_scale"], sched,
+                                 split_ptr)
+    po32, pl32 = po.astype(np.float32), pl.astype(np.float32)
+    ref_out, ref_lse = oracle_combine(po32.astype(np.float64), pl32.astype(np.float64), split_ptr)
+    out, lse = mla.combine(torch.from_numpy(po32).cuda(), torch.from_numpy(pl32).cuda(),
+                           torch.from_numpy(split_ptr).cuda())
+    torch.cuda.synchronize()
+    check_rows(out, lse, ref_out, ref_lse, "combine")
+
+
+def test_combine_all_empty_splits():
+    po = torch.zeros((3, 4, 512), device="cuda")
+    pl = torch.full((3, 4), -math.inf, device="cuda")
+    sp = torch.tensor([0, 2, 3], dtype=torch.int32, device="cuda")
+    out, lse = mla.combine(po, pl, sp)
+    assert torch.all(out == 0) and torch.all(torch.isneginf(lse))
+
+
+def test_validate_indices_counts_out_of_pool_entries():
+    idx = torch.tensor([0, 5, -1, 9, 10, 11, -7, 3], dtype=torch.int32, device="cuda")
+    assert mla.validate_indices(idx, 10) == 2
+    assert mla.validate_indices(idx, 100) == 0
+
+
+# ------------------------------------------------------- full-size workloads, sampled rows checked
+
+@pytest.mark.parametrize("cfg,rows", [(0, None), (1, 8), (2, 12), (3, 8), (4, 2)])
+def test_full_size_workloads_sampled_rows(cfg, rows):
+    w = make_workload(cfg)
+    out, lse, md = _decode(w)
+    spec = w["spec"]
+    nrows = spec.rows
+    pick = list(range(nrows)) if rows is None else sorted(
+        set(np.random.default_rng(cfg).choice(nrows, size=min(rows, nrows), replace=False).tolist())
+        | {0, nrows - 1})
+    ref_out, ref_lse = oracle_decode_rows(w["q_bits"], w["k_cache"], w["indices"],
+                                          w["softmax_scale"], pick, w["extra_k_cache"],
+                                          w["extra_indices"])
+    o = out.reshape(nrows, spec.h_q, 512)[pick]
+    l = lse.reshape(nrows, spec.h_q)[pick]
+    check_rows(o, l, ref_out, ref_lse, f"config {cfg}")
+    # properties that hold at any size, on every row: finite, lse finite where a token is valid
+    assert torch.isfinite(out.float()).all()
+    valid_rows = (torch.from_numpy(w["indices"]).reshape(nrows, -1) >= 0).any(dim=1)
+    assert torch.isfinite(lse.reshape(nrows, -1)[valid_rows.cuda()]).all()

@@ -1,0 +1,227 @@
+"""Benchmark of the sparse MLA decode hot path on one MI355X.
+
+One step = one mla_sparse_decode call over one batch of synthetic input already resident in HBM
+(the decode kernel, plus the log-sum-exp merge kernel when the schedule splits rows); the tile
+scheduler metadata is computed once before the loop, as the method prescribes, and timed separately.
+Successive steps cycle through several independent index sets over the same paged pool, so no step
+re-reads the records of the previous one from cache.
+
+Prints one JSON line: TFLOP/s over valid selected tokens (2 * h_q * (512 + 512) flops per valid
+token and row), KV GB/s, the roofline block for the decode kernel, and the CPU oracle baseline.
+
+  python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--config 2] [--no-cpu-baseline]
+"""
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+METRIC = "sparse MLA decode TFLOP/s + KV GB/s, fp8 528B/tok, B=128 H=128 topk=2048"
+DECODE_SRC = os.path.join(ROOT, "sparse_mla_decode_get_amd", "csrc", "mla_decode.hip")
+
+
+def kernel_source_hash() -> str:
+    return hashlib.sha256(open(DECODE_SRC, "rb").read()).hexdigest()[:16]
+
+
+def stored_traffic(config: int):
+    """HBM bytes per launch measured with rocprofv3 --pmc for this decode kernel source, if the
+    committed counter summary was taken on the current kernel; otherwise None."""
+    path = os.path.join(ROOT, "profiles", f"mla_decode_config{config}_pmc.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_sha = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_sha or not m_b or m_sha.group(1) != kernel_source_hash():
+        return None
+    return float(m_b.group(1))
+
+
+def cpu_baseline(w, seconds: float):
+    """Time the float64 oracle (as it stands) on whole rows of the same workload until `seconds`."""
+    from oracle import oracle_decode_rows
+    spec = w["spec"]
+    rows = spec.rows
+    order = np.random.default_rng(0).permutation(rows)
+    done, flops, kv = 0, 0.0, 0.0
+    idx = w["indices"].reshape(rows, -1)
+    xidx = None if w["extra_indices"] is None else w["extra_indices"].reshape(rows, -1)
+    t0 = time.perf_counter()
+    while done < rows and time.perf_counter() - t0 < seconds:
+        r = int(order[done])
+        oracle_decode_rows(w["q_bits"], w["k_cache"], w["indices"], w["softmax_scale"], [r],
+                           w["extra_k_cache"], w["extra_indices"])
+        nv = int((idx[r] >= 0).sum())
+        nx = 0 if xidx is None else int((xidx[r] >= 0).sum())
+        flops += 2.0 * spec.h_q * 1024 * (nv + nx)
+        kv += 528.0 * nv + 288.0 * nx
+        done += 1
+    dt = time.perf_counter() - t0
+    try:
+        import threadpoolctl
+        threads = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()) \
+            if threadpoolctl.threadpool_info() else 1
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} of {rows} query rows of the same workload (all {spec.h_q} heads each), "
+                      f"{dt:.1f} s wall, float64 NumPy oracle on the host; KV {kv / dt / 1e9:.3f} GB/s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--sets", type=int, default=4, help="independent index sets cycled over steps")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="run one 1 GiB device copy first (calibrates HBM byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
+              "(rows shard across GPUs with no exchange; see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import sparse_mla_decode_get_amd as mla
+    from workloads import CONFIGS, add_index_set, make_workload
+
+    mla.load_library()          # fails loudly when the HIP library is missing
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+
+    t_gen = time.perf_counter()
+    w = make_workload(args.config)
+    spec = w["spec"]
+    sets = [w["indices"]] + [add_index_set(w, 5000 + k) for k in range(args.sets - 1)] \
+        if spec.extra_topk == 0 and spec.order == "random" else [w["indices"]]
+    t_gen = time.perf_counter() - t_gen
+
+    if args.copy_probe:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    q = torch.from_numpy(w["q_bits"].view(np.int16)).view(torch.bfloat16).to(dev)
+    k_cache = torch.from_numpy(w["k_cache"]).to(dev)
+    idx_sets = [torch.from_numpy(s).to(dev) for s in sets]
+    xc = xi = None
+    if w["extra_k_cache"] is not None:
+        xc = torch.from_numpy(w["extra_k_cache"]).to(dev)
+        xi = torch.from_numpy(w["extra_indices"]).to(dev)
+    b, s, h = spec.batch, spec.seq_len_q, spec.h_q
+    out = torch.empty((b, s, h, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((b, s, h), dtype=torch.float32, device=dev)
+
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    md = mla.get_metadata(b, s, h, spec.topk, spec.extra_topk)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    metadata_ms = e0.elapsed_time(e1)
+
+    def step(k):
+        mla.sparse_decode(q, k_cache, idx_sets[k % len(idx_sets)], w["softmax_scale"], md, xc, xi,
+                          out=out, lse=lse)
+
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for k in range(args.steps):
+        starts[k].record(stream)
+        step(k)
+        ends[k].record(stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = e0.elapsed_time(e1)
+    per_launch_ms = float(np.mean([a.elapsed_time(z) for a, z in zip(starts, ends)]))
+    ms_per_step = total_ms / args.steps
+
+    # algorithmic work per step (valid tokens only), averaged over the index sets the steps used
+    nv = np.mean([[(sets[k % len(sets)] >= 0).sum()] for k in range(args.steps)])
+    nx = 0 if w["extra_indices"] is None else float((w["extra_indices"] >= 0).sum())
+    flops = 2.0 * h * 1024 * (nv + nx)
+    kv_bytes = 528.0 * nv + 288.0 * nx
+    rows = b * s
+    alg_bytes = kv_bytes + 4.0 * rows * (spec.topk + spec.extra_topk) + 2 * rows * h * 512 * 2 \
+        + rows * h * 4
+    tflops = flops / (ms_per_step * 1e-3) / 1e12
+    kv_gbs = kv_bytes / (ms_per_step * 1e-3) / 1e9
+    intensity = flops / alg_bytes
+    ridge = BF16_MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if intensity >= ridge:
+        roof = {"bound": "mfma", "achieved": flops / (per_launch_ms * 1e-3) / 1e12,
+                "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": alg_bytes / (per_launch_ms * 1e-3) / 1e9,
+                "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = stored_traffic(args.config)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, args.cpu_seconds)
+
+    line = {
+        "metric": METRIC,
+        "value": tflops,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{spec.name} sparse MLA decode: batch {b}, seq_len_q {s}, h_q {h}, "
+                               f"topk {spec.topk}" + (f" + extra {spec.extra_topk} fp4" if spec.extra_topk else "")
+                               + f", {spec.tokens_per_seq} tokens per sequence in 64-token blocks, "
+                               f"528 B fp8 records",
+                   "batch": b, "seq_len_q": s, "h_q": h, "topk": spec.topk,
+                   "extra_topk": spec.extra_topk, "index_sets": len(sets),
+                   "num_parts": md.num_parts},
+        "kv_gbps": kv_gbs,
+        "alg_gbps": alg_bytes / (ms_per_step * 1e-3) / 1e9,
+        "valid_tokens_per_step": float(nv + nx),
+        "hbm_frac": alg_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "metadata_ms": metadata_ms,
+        "per_launch_ms": per_launch_ms,
+        "wall_s_timed": wall,
+        "gen_s": t_gen,
+        "kernel_source_sha256_16": kernel_source_hash(),
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -5,7 +5,7 @@
 #include <cmath>
 #include <cstdint>
 
-#include "../../include/mla.h"
+#include "mla.h"
 #include "mla_internal.h"
 
 namespace {
@@ -19,8 +19,9 @@ int tiles_per_row(int topk, int extra_topk, int* tiles_k) {
   return tk + tx > 0 ? tk + tx : 1;
 }
 
-// Waves per workgroup: one wave per 16 heads of the head group (32, 64 or 128 heads).
-int waves_for(int h_q) { return h_q <= 32 ? 2 : (h_q <= 64 ? 4 : 8); }
+// Waves per workgroup: one wave per 16 heads of the head group (64 or 128 heads; smaller head
+// counts run in a 64-head group with the extra heads masked).
+int waves_for(int h_q) { return h_q <= 64 ? 4 : 8; }
 int head_groups(int h_q) { return (h_q + 16 * waves_for(h_q) - 1) / (16 * waves_for(h_q)); }
 
 int default_parts(int h_q) {
@@ -30,8 +31,8 @@ int default_parts(int h_q) {
     if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
       cus = v;
   }
-  // workgroups resident per CU: 8-wave groups fill a CU (two waves per SIMD); smaller groups fit
-  // twice (limited by LDS, about 70-75 KB each)
+  // workgroups resident per CU: an 8-wave group fills a CU (two waves per SIMD); 4-wave groups
+  // fit twice (about 75 KB of LDS each)
   const int per_cu = waves_for(h_q) == 8 ? 1 : 2;
   const int parts = cus * per_cu / head_groups(h_q);
   return parts > 0 ? parts : 1;

@@ -8,7 +8,7 @@
 //
 // Work decomposition. The grid is (parts, head groups). A workgroup takes the contiguous range of
 // (row, 64-slot unit) work the tile-scheduler metadata gives its part, for HG query heads
-// (HG = 32, 64 or 128) with W = HG / 16 waves, two waves per SIMD. Every wave has the same register
+// (HG = 64 or 128) with W = HG / 16 waves, two waves per SIMD. Every wave has the same register
 // footprint: Q of 16 heads (64 VGPRs) and an fp32 output accumulator of 8 MFMA blocks (128 AGPRs).
 // Each 64-slot unit runs as two sub-tiles of 32 tokens:
 //   1. gather   all lanes copy 16-byte chunks of the selected records (data and scales together,
@@ -66,10 +66,11 @@ __device__ __forceinline__ void lds_write16(char* base, int off, u32x4 v) {
 }
 
 // Index entry of token `tok` of sub-tile `s` in the unit range that starts at unit `t0` of `row`.
+template <bool EXTRA>
 __device__ __forceinline__ int load_index(const DecodeParams& p, int row, int t0, int s, int tok) {
   const int unit = t0 + (s >> 1);
   const int half = s & 1;
-  if (unit < p.tiles_k) {
+  if (!EXTRA || unit < p.tiles_k) {
     const int pos = unit * kUnitTokens + half * kSubTokens + tok;
     return pos < p.topk ? p.idx[(int64_t)row * p.topk + pos] : -1;
   }
@@ -77,7 +78,11 @@ __device__ __forceinline__ int load_index(const DecodeParams& p, int row, int t0
   return pos < p.extra_topk ? p.xidx[(int64_t)row * p.extra_topk + pos] : -1;
 }
 
-__device__ __forceinline__ float xor16(float v) { return __shfl_xor(v, 16); }
+// Value of lane (lane ^ 16); `lane` is the caller's (opaque) lane id.
+__device__ __forceinline__ float xor16(float v, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((lane ^ 16) << 2,
+                                                                __builtin_bit_cast(int, v)));
+}
 
 // Lane id from the exec-mask counters (cheap to recompute anywhere).
 // The empty asm makes each call's result opaque, so the compiler recomputes lane-derived offsets
@@ -99,9 +104,29 @@ __device__ __forceinline__ void barrier_lds() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-typedef __attribute__((address_space(3))) void lds_void;
+// One lane's 16-byte global -> LDS copy (global_load_lds_dwordx4): the wave's active lanes write
+// LDS bytes m0 + 16 * lane. Issued as inline asm so that the compiler does not treat every later LDS
+// read as possibly aliasing it (which would make it wait for the copy right away); completion is
+// awaited explicitly by barrier_all's vmcnt(0). m0 is saved and restored around the copy, and
+// `lds_base` must be wave-uniform.
+__device__ __forceinline__ void copy16_to_lds(const void* gptr, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_base), "v"(gptr)
+      : "memory");
+}
 
-template <int W>
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+template <int W, bool EXTRA>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void sparse_decode_kernel(DecodeParams p) {
   using C = DecodeCfg<W>;
@@ -120,14 +145,17 @@ void sparse_decode_kernel(DecodeParams p) {
   float* lfin_s = reinterpret_cast<float*>(smem + C::kOffLFin);
   int* flag_s = reinterpret_cast<int*>(smem + C::kOffFlag);
 
+  // This part's units run from (sc[0], sc[1]) to the exclusive end (sc[2], sc[3]); they are walked
+  // row segment by row segment without any division.
   const int32_t* sc = p.sched + blockIdx.x * 8;
-  const int64_t tiles = p.tiles;
-  int64_t u = (int64_t)sc[0] * tiles + sc[1];
-  const int64_t u_end = (int64_t)sc[2] * tiles + sc[3];
+  int row = sc[0];
+  int t0 = sc[1];
+  const int end_row = sc[2];
+  const int end_tile = sc[3];
   const int slot_first = sc[4];
   bool first_seg = true;
 
-  while (u < u_end) {
+  while (row < end_row || (row == end_row && t0 < end_tile)) {
     // Lane-derived indices are recomputed from an opaque copy of the lane id in each row segment
     // (and again in each sub-tile below) rather than kept live across the whole kernel.
     int lane = lane_id();
@@ -138,28 +166,22 @@ void sparse_decode_kernel(DecodeParams p) {
     // QK^T role: lane (t16, q4) holds Q of head my_head for dims 64c + 16*q4 .. +15.
     const int my_head = head_base + 16 * wave + t16;
 
-    const int row = (int)(u / tiles);
-    const int t0 = (int)(u - (int64_t)row * tiles);
-    const int64_t seg_end = min(u_end, (int64_t)(row + 1) * tiles);
-    const int nsub = 2 * (int)(seg_end - u);
+    const int t1 = row < end_row ? p.tiles : end_tile;
+    const int nsub = 2 * (t1 - t0);
     const int split_base = p.split_ptr[row];
     const int nsplit = p.split_ptr[row + 1] - split_base;
     const int slot = first_seg ? slot_first : split_base;
 
+    // Q (B operand): heads past h_q load a copy of the last head; their results are never stored.
     bf16x8 qreg[8][2];
-    if (my_head < p.h_q) {
+    {
+      const int qh = min(my_head, p.h_q - 1);
       const u32x4* qp = reinterpret_cast<const u32x4*>(
-          p.q + ((int64_t)row * p.h_q + my_head) * kHeadDim + 16 * q4);
+          p.q + ((int64_t)row * p.h_q + qh) * kHeadDim + 16 * q4);
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
         qreg[c][0] = __builtin_bit_cast(bf16x8, qp[8 * c]);
         qreg[c][1] = __builtin_bit_cast(bf16x8, qp[8 * c + 1]);
-      }
-    } else {
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        qreg[c][0] = bf16x8{};
-        qreg[c][1] = bf16x8{};
       }
     }
 
@@ -176,11 +198,12 @@ void sparse_decode_kernel(DecodeParams p) {
     // lanes whose token is ignored, and lanes past the record, issue nothing.
     auto issue = [&](int s, int my_idx, char* buf, bool& is_fp4) -> uint32_t {
       const int unit = t0 + (s >> 1);
-      is_fp4 = unit >= p.tiles_k;
+      is_fp4 = EXTRA && unit >= p.tiles_k;
       const bool valid = my_idx >= 0;
       const uint32_t bal = (uint32_t)__ballot(valid);   // lanes 0..31 carry tokens 0..31
       const int nq = is_fp4 ? (kFp4Chunks / 2) : 17;
       const int nch = is_fp4 ? kFp4Chunks : kFp8Chunks;
+      const uint32_t buf_lds = __builtin_amdgcn_readfirstlane(lds_addr(buf));
       // per-lane record pointer, already advanced to this lane's chunk of each chunk pair
       const uint8_t* lane_base = (is_fp4 ? p.xc + (int64_t)(valid ? my_idx : 0) * kFp4Rec
                                          : p.kc + (int64_t)(valid ? my_idx : 0) * kFp8Rec) + 16 * hh;
@@ -188,22 +211,22 @@ void sparse_decode_kernel(DecodeParams p) {
       for (int j = 0; j < C::kNQ; ++j) {
         const int qi = wave + W * j;                      // uniform: chunks 2qi (+0) and 2qi+1 (+16)
         if (qi < nq) {
+          const uint32_t dst = __builtin_amdgcn_readfirstlane(buf_lds + 1024 * qi);
           const bool ok = valid && (2 * qi + 1 < nch || hh == 0);
-          if (ok)
-            __builtin_amdgcn_global_load_lds(lane_base + 32 * qi, (lds_void*)(buf + 1024 * qi), 16, 0, 0);
+          if (ok) copy16_to_lds(lane_base + 32 * qi, dst);
         }
       }
       return bal;
     };
 
-    int idx_cur = load_index(p, row, t0, 0, tok);
+    int idx_cur = load_index<EXTRA>(p, row, t0, 0, tok);
     bool fp4_next = false;
     uint32_t mask_next = issue(0, idx_cur, raw0, fp4_next);
-    int idx_next = nsub > 1 ? load_index(p, row, t0, 1, tok) : -1;
+    int idx_next = nsub > 1 ? load_index<EXTRA>(p, row, t0, 1, tok) : -1;
 
     auto step = [&](int s, char* raw, char* raw_other) {
       const uint32_t mask = mask_next;
-      const bool is_fp4 = fp4_next;
+      const bool is_fp4 = EXTRA && fp4_next;
       const int lane = lane_id();
       const int tok = lane & 31;
       const int hh = lane >> 5;
@@ -212,56 +235,97 @@ void sparse_decode_kernel(DecodeParams p) {
       barrier_all();
       if (s + 1 < nsub) {
         mask_next = issue(s + 1, idx_next, raw_other, fp4_next);
-        idx_next = (s + 2 < nsub) ? load_index(p, row, t0, s + 2, tok) : -1;
+        idx_next = (s + 2 < nsub) ? load_index<EXTRA>(p, row, t0, s + 2, tok) : -1;
       }
       if (mask != 0) {
-        // ---------------- QK^T with in-register dequant; this wave's V slice to LDS
-        f32x4 sacc[2];
+        // ---------------- QK^T with in-register dequant (two token blocks, two MFMA chains).
+        // The LDS read of step c+1 is issued before step c is converted; the scheduling barrier
+        // keeps the compiler from hoisting every read of the loop (which would exhaust registers).
+        f32x4 sacc[2] = {f32x4{}, f32x4{}};
+        if (!is_fp4) {
+          u32x4 scl[2], rn[2];
+#pragma unroll
+          for (int tb = 0; tb < 2; ++tb) {
+            scl[tb] = lds_read16(raw, (32 * kSubTokens + 16 * tb + t16) * 16);   // e8m0 scales
+            rn[tb] = lds_read16(raw, ((0 + q4) * kSubTokens + 16 * tb + t16) * 16);
+          }
+#pragma unroll
+          for (int c = 0; c < 8; ++c) {
+            u32x4 r[2] = {rn[0], rn[1]};
+            if (c + 1 < 8) {
+#pragma unroll
+              for (int tb = 0; tb < 2; ++tb)
+                rn[tb] = lds_read16(raw, ((4 * (c + 1) + q4) * kSubTokens + 16 * tb + t16) * 16);
+            }
+            const int blk = 2 * c + (q4 >> 1);                                // 32-dim scale block
+#pragma unroll
+            for (int tb = 0; tb < 2; ++tb) {
+              const uint32_t sb = (scl[tb][blk >> 2] >> (8 * (blk & 3))) & 0xFFu;
+              bf16x8 a0, a1;
+              dequant_fp8_16(r[tb], sb, a0, a1);
+              sacc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qreg[c][0], sacc[tb], 0, 0, 0);
+              sacc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qreg[c][1], sacc[tb], 0, 0, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        } else {
+          u32x2 rn[2];
+#pragma unroll
+          for (int tb = 0; tb < 2; ++tb)
+            rn[tb] = *reinterpret_cast<const u32x2*>(
+                raw + ((q4 >> 1) * kSubTokens + 16 * tb + t16) * 16 + 8 * (q4 & 1));
+#pragma unroll
+          for (int c = 0; c < 8; ++c) {
+            // dims 64c + 16*q4 .. +15 = bytes 32c + 8*q4 .. +7 = chunk 2c + q4/2, offset 8*(q4&1);
+            // their e4m3 scale is byte j % 16 of chunk 16 + j / 16, j = 4c + q4
+            u32x2 r[2] = {rn[0], rn[1]};
+            if (c + 1 < 8) {
+#pragma unroll
+              for (int tb = 0; tb < 2; ++tb)
+                rn[tb] = *reinterpret_cast<const u32x2*>(
+                    raw + ((2 * (c + 1) + (q4 >> 1)) * kSubTokens + 16 * tb + t16) * 16 + 8 * (q4 & 1));
+            }
+            const int j = 4 * c + q4;
+#pragma unroll
+            for (int tb = 0; tb < 2; ++tb) {
+              const uint32_t sb = *reinterpret_cast<const uint8_t*>(
+                  raw + ((16 + (j >> 4)) * kSubTokens + 16 * tb + t16) * 16 + (j & 15));
+              bf16x8 a0, a1;
+              dequant_fp4_16(r[tb][0], r[tb][1], e4m3_to_f32(sb), a0, a1);
+              sacc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qreg[c][0], sacc[tb], 0, 0, 0);
+              sacc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qreg[c][1], sacc[tb], 0, 0, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+
+        // ---------------- this wave's PV dim slice of the same tokens, dequantized for the V operand
+        // (zero for ignored tokens) into the wave's private LDS slice, token-major.
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb) {
-          const int t = 16 * tb + t16;                      // token of this lane's A operand
+          const int t = 16 * tb + t16;
           const bool tok_valid = (mask >> t) & 1u;
-          f32x4 acc = f32x4{};
-          if (!is_fp4) {
-            const u32x4 scl = lds_read16(raw, (32 * kSubTokens + t) * 16);   // 16 e8m0 scales
 #pragma unroll
-            for (int c = 0; c < 8; ++c) {
-              const int blk = 2 * c + (q4 >> 1);                              // 32-dim scale block
+          for (int cs = 0; cs < C::kSlice / 64; ++cs) {
+            const int c = wave * (C::kSlice / 64) + cs;                       // uniform
+            bf16x8 a0, a1;
+            if (!is_fp4) {
               const u32x4 r = lds_read16(raw, ((4 * c + q4) * kSubTokens + t) * 16);
-              const uint32_t sb = (scl[blk >> 2] >> (8 * (blk & 3))) & 0xFFu;
-              bf16x8 a0, a1;
+              const uint32_t sb = *reinterpret_cast<const uint8_t*>(
+                  raw + (32 * kSubTokens + t) * 16 + 2 * c + (q4 >> 1));   // e8m0 of the block
               dequant_fp8_16(r, sb, a0, a1);
-              acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qreg[c][0], acc, 0, 0, 0);
-              acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qreg[c][1], acc, 0, 0, 0);
-              if ((64 * c) / C::kSlice == wave) {
-                const int off = t * C::kVStride + (64 * c - wave * C::kSlice + 16 * q4) * 2;
-                lds_write16(vslice, off, tok_valid ? __builtin_bit_cast(u32x4, a0) : u32x4{});
-                lds_write16(vslice, off + 16, tok_valid ? __builtin_bit_cast(u32x4, a1) : u32x4{});
-              }
-            }
-          } else {
-            const u32x4 s0 = lds_read16(raw, (16 * kSubTokens + t) * 16);    // e4m3 scales 0..15
-            const u32x4 s1 = lds_read16(raw, (17 * kSubTokens + t) * 16);    // scales 16..31
-#pragma unroll
-            for (int c = 0; c < 8; ++c) {
-              // dims 64c + 16*q4 .. +15 = bytes 32c + 8*q4 .. +7 = chunk 2c + q4/2, offset 8*(q4&1)
+            } else {
               const u32x2 r = *reinterpret_cast<const u32x2*>(
                   raw + ((2 * c + (q4 >> 1)) * kSubTokens + t) * 16 + 8 * (q4 & 1));
-              const int j = 4 * c + q4;                                       // 16-dim scale index
-              const u32x4 sv = (c < 4) ? s0 : s1;
-              const uint32_t sb = (sv[(j & 15) >> 2] >> (8 * (j & 3))) & 0xFFu;
-              bf16x8 a0, a1;
+              const int j = 4 * c + q4;
+              const uint32_t sb = *reinterpret_cast<const uint8_t*>(
+                  raw + ((16 + (j >> 4)) * kSubTokens + t) * 16 + (j & 15));
               dequant_fp4_16(r[0], r[1], e4m3_to_f32(sb), a0, a1);
-              acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qreg[c][0], acc, 0, 0, 0);
-              acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qreg[c][1], acc, 0, 0, 0);
-              if ((64 * c) / C::kSlice == wave) {
-                const int off = t * C::kVStride + (64 * c - wave * C::kSlice + 16 * q4) * 2;
-                lds_write16(vslice, off, tok_valid ? __builtin_bit_cast(u32x4, a0) : u32x4{});
-                lds_write16(vslice, off + 16, tok_valid ? __builtin_bit_cast(u32x4, a1) : u32x4{});
-              }
             }
+            const int off = t * C::kVStride + (64 * cs + 16 * q4) * 2;
+            lds_write16(vslice, off, tok_valid ? __builtin_bit_cast(u32x4, a0) : u32x4{});
+            lds_write16(vslice, off + 16, tok_valid ? __builtin_bit_cast(u32x4, a1) : u32x4{});
           }
-          sacc[tb] = acc;
         }
 
         // ---------------- online softmax for head 16*wave + t16; sacc[tb][i] is token 16tb+4q4+i
@@ -277,7 +341,7 @@ void sparse_decode_kernel(DecodeParams p) {
             x[4 * tb + i] = v;
             mx = fmaxf(mx, v);
           }
-        mx = fmaxf(mx, xor16(mx));
+        mx = fmaxf(mx, xor16(mx, lane));
         mx = max_xor32(mx);
         const float m_new = fmaxf(m_run, mx);
         const bool resc = m_new > m_run + 8.0f;    // also true for the first sub-tile with a token
@@ -300,7 +364,7 @@ void sparse_decode_kernel(DecodeParams p) {
           }
           *reinterpret_cast<bf16x4*>(prow + (16 * tb + 4 * q4) * 2) = pk;
         }
-        ls += xor16(ls);
+        ls += xor16(ls, lane);
         ls = sum_xor32(ls);
         l_run = l_run * alpha + ls;
         const uint64_t any_resc = __ballot(resc);
@@ -320,28 +384,38 @@ void sparse_decode_kernel(DecodeParams p) {
           }
         }
         const int g = lane >> 4, j = lane & 15;
+        typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+        // V^T operand for (ks, d): two transposed reads of the private slice, lane (dim, 8 tokens)
+        auto load_v = [&](int ks, int d) -> bf16x8 {
+          const int row0 = 16 * ks + 8 * (g >> 1) + (j >> 2);
+          const int col = 32 * d + 16 * (g & 1) + 4 * (j & 3);
+          const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+              (lds_bf16x4*)(vslice + row0 * C::kVStride + col * 2));
+          const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+              (lds_bf16x4*)(vslice + (row0 + 4) * C::kVStride + col * 2));
+          return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+        };
+        bf16x8 av_next = load_v(0, 0);
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
+          bf16x8 pb[C::kHB];
+#pragma unroll
+          for (int b = 0; b < C::kHB; ++b)
+            pb[b] = *reinterpret_cast<const bf16x8*>(
+                pbuf + (32 * b + (lane & 31)) * C::kPStride + (16 * ks + 8 * hh) * 2);
 #pragma unroll
           for (int d = 0; d < C::kDB; ++d) {
-            const int row0 = 16 * ks + 8 * (g >> 1) + (j >> 2);
-            const int col = 32 * d + 16 * (g & 1) + 4 * (j & 3);
-            typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
-            const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                (lds_bf16x4*)(vslice + row0 * C::kVStride + col * 2));
-            const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                (lds_bf16x4*)(vslice + (row0 + 4) * C::kVStride + col * 2));
-            const bf16x8 av = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+            const bf16x8 av = av_next;
+            if (d + 1 < C::kDB) av_next = load_v(ks, d + 1);
+            else if (ks == 0) av_next = load_v(1, 0);
 #pragma unroll
-            for (int b = 0; b < C::kHB; ++b) {
-              const bf16x8 pb = *reinterpret_cast<const bf16x8*>(
-                  pbuf + (32 * b + (lane & 31)) * C::kPStride + (16 * ks + 8 * hh) * 2);
-              oacc[d][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb, oacc[d][b], 0, 0, 0);
-            }
+            for (int b = 0; b < C::kHB; ++b)
+              oacc[d][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[b], oacc[d][b], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
           }
         }
       }
-        };
+    };
 
     for (int s = 0; s < nsub; s += 2) {
       step(s, raw0, raw1);
@@ -385,26 +459,30 @@ void sparse_decode_kernel(DecodeParams p) {
         }
       }
     }
-    if (q4e == 0 && my_head < p.h_q) {
+    const int head_e = head_base + 16 * wave + t16e;
+    if (q4e == 0 && head_e < p.h_q) {
       const float lse = l_run > 0.0f ? (m_run + __log2f(l_run)) * 0.69314718055994530942f
                                      : -__builtin_inff();
       if (final_out)
-        p.lse[(int64_t)row * p.h_q + my_head] = lse;
+        p.lse[(int64_t)row * p.h_q + head_e] = lse;
       else
-        p.part_lse[(int64_t)slot * p.h_q + my_head] = lse;
+        p.part_lse[(int64_t)slot * p.h_q + head_e] = lse;
     }
     __syncthreads();
-    u = seg_end;
+    ++row;
+    t0 = 0;
     first_seg = false;
   }
 }
 
 int launch_sparse_decode(const DecodeParams& p, int parts, int groups, int waves, hipStream_t stream) {
   dim3 grid(parts, groups);
-  switch (waves) {
-    case 8: hipLaunchKernelGGL(sparse_decode_kernel<8>, grid, dim3(512), 0, stream, p); break;
-    case 4: hipLaunchKernelGGL(sparse_decode_kernel<4>, grid, dim3(256), 0, stream, p); break;
-    case 2: hipLaunchKernelGGL(sparse_decode_kernel<2>, grid, dim3(128), 0, stream, p); break;
+  const bool extra = p.extra_topk > 0;
+  switch (waves * 2 + (extra ? 1 : 0)) {
+    case 16: hipLaunchKernelGGL((sparse_decode_kernel<8, false>), grid, dim3(512), 0, stream, p); break;
+    case 17: hipLaunchKernelGGL((sparse_decode_kernel<8, true>), grid, dim3(512), 0, stream, p); break;
+    case 8: hipLaunchKernelGGL((sparse_decode_kernel<4, false>), grid, dim3(256), 0, stream, p); break;
+    case 9: hipLaunchKernelGGL((sparse_decode_kernel<4, true>), grid, dim3(256), 0, stream, p); break;
     default: return -1;
   }
   return hipGetLastError() == hipSuccess ? 0 : -1;

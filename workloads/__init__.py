@@ -211,3 +211,22 @@ def make_workload(spec: Spec | int, seed: int | None = None, encode_chunk: int =
     return dict(spec=spec, q_bits=q_bits, k_cache=k_cache, indices=indices,
                 extra_k_cache=extra_k_cache, extra_indices=extra_indices,
                 softmax_scale=spec.softmax_scale)
+
+
+def add_index_set(w: dict, seed: int, encode_chunk: int = 65536) -> np.ndarray:
+    """Draw another fp8 index set for the same rows and shapes as workload `w` (new distinct positions,
+    same -1 rule), encode the newly selected records into w["k_cache"] in place, and return the
+    int32 [B, S, topk] indices. Used to give successive benchmark steps different tokens."""
+    spec = w["spec"]
+    b_, s_ = spec.batch, spec.seq_len_q
+    rng_t, rng_i, rng_c = [np.random.default_rng(x) for x in np.random.SeedSequence(seed).spawn(3)]
+    blocks_per_seq = -(-spec.tokens_per_seq // BLOCK)
+    table = rng_t.permutation(b_ * blocks_per_seq).reshape(b_, blocks_per_seq)
+    phys = _select(rng_i, None, b_, s_, spec.topk, spec.tokens_per_seq, spec.order, table)
+    idx = _apply_neg(rng_i, phys, spec.neg)
+    pool = w["k_cache"]
+    sel = np.unique(idx[idx >= 0])
+    for a in range(0, sel.size, encode_chunk):
+        part = sel[a:a + encode_chunk]
+        pool[part] = encode_fp8_records(_values(rng_c, part.size, spec.values))
+    return idx.astype(np.int32).reshape(b_, s_, spec.topk)

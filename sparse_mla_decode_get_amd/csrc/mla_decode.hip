@@ -131,8 +131,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void sparse_decode_kernel(DecodeParams p) {
   using C = DecodeCfg<W>;
   __shared__ __attribute__((aligned(16))) char smem[C::kLdsBytes];
-  __shared__ __attribute__((aligned(16))) char raw0[C::kRawBytes];
-  __shared__ __attribute__((aligned(16))) char raw1[C::kRawBytes];
+  __shared__ __attribute__((aligned(16))) char rawbuf[2 * C::kRawBytes];   // double-buffered records
 
   // The wave index is uniform: keep it (and everything derived from it) in scalar registers.
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -172,6 +171,7 @@ void sparse_decode_kernel(DecodeParams p) {
     const int nsplit = p.split_ptr[row + 1] - split_base;
     const int slot = first_seg ? slot_first : split_base;
 
+    // Q (B operand): heads past h_q load a copy of the last head; their results are never stored.
     // Q (B operand): heads past h_q load a copy of the last head; their results are never stored.
     bf16x8 qreg[8][2];
     {
@@ -221,10 +221,12 @@ void sparse_decode_kernel(DecodeParams p) {
 
     int idx_cur = load_index<EXTRA>(p, row, t0, 0, tok);
     bool fp4_next = false;
-    uint32_t mask_next = issue(0, idx_cur, raw0, fp4_next);
+    uint32_t mask_next = issue(0, idx_cur, rawbuf, fp4_next);
     int idx_next = nsub > 1 ? load_index<EXTRA>(p, row, t0, 1, tok) : -1;
 
-    auto step = [&](int s, char* raw, char* raw_other) {
+    for (int s = 0; s < nsub; ++s) {
+      char* raw = rawbuf + (s & 1) * C::kRawBytes;
+      char* raw_other = rawbuf + ((s + 1) & 1) * C::kRawBytes;
       const uint32_t mask = mask_next;
       const bool is_fp4 = EXTRA && fp4_next;
       const int lane = lane_id();
@@ -244,6 +246,7 @@ void sparse_decode_kernel(DecodeParams p) {
         f32x4 sacc[2] = {f32x4{}, f32x4{}};
         if (!is_fp4) {
           u32x4 scl[2], rn[2];
+          const uint32_t sc_shift = 8 * (q4 >> 1);
 #pragma unroll
           for (int tb = 0; tb < 2; ++tb) {
             scl[tb] = lds_read16(raw, (32 * kSubTokens + 16 * tb + t16) * 16);   // e8m0 scales
@@ -257,10 +260,11 @@ void sparse_decode_kernel(DecodeParams p) {
               for (int tb = 0; tb < 2; ++tb)
                 rn[tb] = lds_read16(raw, ((4 * (c + 1) + q4) * kSubTokens + 16 * tb + t16) * 16);
             }
-            const int blk = 2 * c + (q4 >> 1);                                // 32-dim scale block
+            // 32-dim scale block 2c + q4/2: word c/2 of the 16 scale bytes (a constant index),
+            // byte 2(c&1) + q4/2 inside it (a per-lane shift)
 #pragma unroll
             for (int tb = 0; tb < 2; ++tb) {
-              const uint32_t sb = (scl[tb][blk >> 2] >> (8 * (blk & 3))) & 0xFFu;
+              const uint32_t sb = __builtin_amdgcn_ubfe(scl[tb][c >> 1], 16 * (c & 1) + sc_shift, 8);
               bf16x8 a0, a1;
               dequant_fp8_16(r[tb], sb, a0, a1);
               sacc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qreg[c][0], sacc[tb], 0, 0, 0);
@@ -415,11 +419,6 @@ void sparse_decode_kernel(DecodeParams p) {
           }
         }
       }
-    };
-
-    for (int s = 0; s < nsub; s += 2) {
-      step(s, raw0, raw1);
-      if (s + 1 < nsub) step(s + 1, raw1, raw0);
     }
     __syncthreads();
 

@@ -27,11 +27,16 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 METRIC = "sparse MLA decode TFLOP/s + KV GB/s, fp8 528B/tok, B=128 H=128 topk=2048"
-DECODE_SRC = os.path.join(ROOT, "sparse_mla_decode_get_amd", "csrc", "mla_decode.hip")
+DECODE_SRCS = [os.path.join(ROOT, "sparse_mla_decode_get_amd", "csrc", f)
+               for f in ("mla_decode_wide.hip", "mla_decode.hip")]
 
 
 def kernel_source_hash() -> str:
-    return hashlib.sha256(open(DECODE_SRC, "rb").read()).hexdigest()[:16]
+    """Hash of the decode kernel sources (the stored counter traffic is valid only for them)."""
+    h = hashlib.sha256()
+    for f in DECODE_SRCS:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def stored_traffic(config: int):

@@ -6,6 +6,10 @@ and no spilled VGPRs, unless MLA_SKIP_REG_SPILL_CHECK=1 is set. SGPR spills are 
 while scratch stays at zero: on gfx950 they go to spare VGPR lanes (v_writelane / v_readlane) and
 never reach memory. The per-kernel report is written to _build/kernel_resources.txt.
 
+Sources whose kernels contain MFMAs written as inline assembly are also compiled to device
+assembly and checked for the wait states gfx950 requires around those MFMAs (asm_check.py); the
+build fails on any violation.
+
 Usage: python -m sparse_mla_decode_get_amd.build   (or build() from Python)
 """
 import concurrent.futures
@@ -19,7 +23,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmla.so")
-SOURCES = ["mla_decode.hip", "mla_sched.hip", "mla_combine.hip", "mla_aux.hip", "mla_api.cpp"]
+SOURCES = ["mla_decode.hip", "mla_decode_wide.hip", "mla_sched.hip", "mla_combine.hip", "mla_aux.hip", "mla_api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = [
@@ -30,8 +34,35 @@ FLAGS = [
 ]
 
 
+# source -> kernel-name fragment whose assembly is checked by asm_check
+ASM_CHECKED = {"mla_decode_wide.hip": "sparse_decode_wide_kernel"}
+
+
 class SpillError(RuntimeError):
     pass
+
+
+class HazardError(RuntimeError):
+    pass
+
+
+def _asm_check(src, name_part):
+    """Compile `src` to gfx950 device assembly and check its inline-assembly MFMAs' wait states."""
+    sys.path.insert(0, PKG)
+    import asm_check
+    out = os.path.join(BUILD, os.path.basename(src) + ".s")
+    cmd = [HIPCC, *FLAGS, "--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", out]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc -S failed for {src}:\n{r.stderr}")
+    text = open(out).read()
+    names = asm_check.kernels(text, name_part)
+    if not names:
+        raise HazardError(f"no kernel matching {name_part} in {src}")
+    problems = []
+    for k in names:
+        problems += [f"{k}: {m}" for m in asm_check.check(text, k)]
+    return problems
 
 
 def _compile(src):
@@ -72,8 +103,12 @@ def _parse_resources(text):
 
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES) + len(ASM_CHECKED)) as ex:
+        checks = [ex.submit(_asm_check, src, part) for src, part in ASM_CHECKED.items()]
         results = list(ex.map(_compile, SOURCES))
+        hazards = [m for c in checks for m in c.result()]
+    if hazards:
+        raise HazardError("MFMA wait-state violations:\n" + "\n".join(hazards[:20]))
     report = {}
     for _, err in results:
         report.update(_parse_resources(err))

@@ -19,10 +19,12 @@ int tiles_per_row(int topk, int extra_topk, int* tiles_k) {
   return tk + tx > 0 ? tk + tx : 1;
 }
 
-// Waves per workgroup: one wave per 16 heads of the head group (64 or 128 heads; smaller head
-// counts run in a 64-head group with the extra heads masked).
-int waves_for(int h_q) { return h_q <= 64 ? 4 : 8; }
-int head_groups(int h_q) { return (h_q + 16 * waves_for(h_q) - 1) / (16 * waves_for(h_q)); }
+// Kernel choice: head counts above 64 run in 128-head groups (mla_decode_wide.hip: four waves of
+// 32 heads, one workgroup per CU); up to 64 heads run in one 64-head group of four waves of 16
+// heads (mla_decode.hip), with heads past h_q masked.
+bool wide_for(int h_q) { return h_q > 64; }
+int group_heads(int h_q) { return wide_for(h_q) ? 128 : 64; }
+int head_groups(int h_q) { return (h_q + group_heads(h_q) - 1) / group_heads(h_q); }
 
 int default_parts(int h_q) {
   int dev = 0, cus = 256;
@@ -31,9 +33,9 @@ int default_parts(int h_q) {
     if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
       cus = v;
   }
-  // workgroups resident per CU: an 8-wave group fills a CU (two waves per SIMD); 4-wave groups
-  // fit twice (about 75 KB of LDS each)
-  const int per_cu = waves_for(h_q) == 8 ? 1 : 2;
+  // workgroups resident per CU: a 128-head group uses about 150 KB of LDS and all registers of
+  // its CU; 64-head groups fit twice (about 75 KB of LDS each)
+  const int per_cu = wide_for(h_q) ? 1 : 2;
   const int parts = cus * per_cu / head_groups(h_q);
   return parts > 0 ? parts : 1;
 }
@@ -175,8 +177,9 @@ int mla_sparse_decode(const void* q, const uint8_t* k_cache, int64_t k_tokens,
   p.out = static_cast<uint16_t*>(out);
   p.lse = lse;
   hipStream_t s = (hipStream_t)stream;
-  if (mla::launch_sparse_decode(p, num_parts_used, head_groups(h_q), waves_for(h_q), s) != 0)
-    return MLA_ERR_HIP;
+  const int launched = wide_for(h_q) ? mla::launch_sparse_decode_wide(p, num_parts_used, head_groups(h_q), s)
+                                     : mla::launch_sparse_decode(p, num_parts_used, head_groups(h_q), 4, s);
+  if (launched != 0) return MLA_ERR_HIP;
   if (split && mla::launch_combine(part_o, part_lse, split_ptr, rows, h_q, p.out, lse, true, s) != 0)
     return MLA_ERR_HIP;
   return MLA_OK;

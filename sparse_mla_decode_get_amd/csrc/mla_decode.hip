@@ -1,4 +1,5 @@
-// Sparse MLA decode kernel for gfx950 (MI355X).
+// Sparse MLA decode kernel for gfx950 (MI355X), 64-head groups (h_q <= 64; larger head counts use
+// the 128-head kernel in mla_decode_wide.hip).
 //
 // What it computes (page "flops/flashmla-decode-fp8-fp4-kv", sections "Arithmetic intensity" and
 // "Workarounds"; page "deepseek-ai/FlashMLA", sections "How to use it" and "Key technical details"):
@@ -8,8 +9,8 @@
 //
 // Work decomposition. The grid is (parts, head groups). A workgroup takes the contiguous range of
 // (row, 64-slot unit) work the tile-scheduler metadata gives its part, for HG query heads
-// (HG = 64 or 128) with W = HG / 16 waves, two waves per SIMD. Every wave has the same register
-// footprint: Q of 16 heads (64 VGPRs) and an fp32 output accumulator of 8 MFMA blocks (128 AGPRs).
+// (HG = 64 here) with W = HG / 16 = 4 waves. Every wave has the same register
+// footprint: Q of 16 heads (64 VGPRs) and an fp32 output accumulator of 8 MFMA blocks.
 // Each 64-slot unit runs as two sub-tiles of 32 tokens:
 //   1. gather   all lanes copy 16-byte chunks of the selected records (data and scales together,
 //               one contiguous record per token) straight from HBM into LDS with
@@ -478,8 +479,6 @@ int launch_sparse_decode(const DecodeParams& p, int parts, int groups, int waves
   dim3 grid(parts, groups);
   const bool extra = p.extra_topk > 0;
   switch (waves * 2 + (extra ? 1 : 0)) {
-    case 16: hipLaunchKernelGGL((sparse_decode_kernel<8, false>), grid, dim3(512), 0, stream, p); break;
-    case 17: hipLaunchKernelGGL((sparse_decode_kernel<8, true>), grid, dim3(512), 0, stream, p); break;
     case 8: hipLaunchKernelGGL((sparse_decode_kernel<4, false>), grid, dim3(256), 0, stream, p); break;
     case 9: hipLaunchKernelGGL((sparse_decode_kernel<4, true>), grid, dim3(256), 0, stream, p); break;
     default: return -1;

@@ -1,0 +1,998 @@
+// Sparse MLA decode kernel for gfx950, 128-head groups (h_q > 64).
+//
+// Same computation as the kernel in mla_decode.hip (page "flops/flashmla-decode-fp8-fp4-kv",
+// sections "Arithmetic intensity" and "Workarounds"; page "deepseek-ai/FlashMLA", section "Key
+// technical details"): per query row and head, one softmax over the row's selected tokens, key and
+// value both the 512-dim latent decoded from the token's quantized record, negative indices ignored,
+// natural-log lse returned beside the output.
+//
+// Layout of the work. One workgroup = 4 waves = one wave per SIMD, each wave with the full 512
+// registers of its SIMD. Wave w owns query heads 32w..32w+31 of the head group for everything:
+//   Q      bf16, 32 heads x 512 dims, 128 VGPRs (B operand of the QK^T product)
+//   O^T    fp32, 512 dims x 32 heads, 16 MFMA blocks of 32x32 = all 256 AGPRs
+//   S^T    fp32, 32 tokens x 32 heads per 32-token sub-tile, 16 VGPRs
+// so the softmax (max, exp, sum, P) never leaves the wave: P goes from the QK^T accumulator layout
+// to the PV operand layout with v_permlane32_swap, no LDS round trip and no cross-wave exchange.
+//
+// Each selected record is gathered once (HBM -> LDS with global_load_lds_dwordx4) and dequantized
+// once, by all four waves together (each takes 128 dims), into a bf16 tile [32 tokens][512 dims]
+// that both products read: QK^T as row reads (ds_read_b128), PV as transposed reads
+// (ds_read_b64_tr_b16). Three tiles and three raw buffers rotate through a software pipeline in
+// which iteration s, behind a single workgroup barrier,
+//   - loads the indices of sub-tile s+6 and gathers the records of sub-tile s+4,
+//   - runs QK^T of sub-tile s+1 (one assembly block: the scores land in VGPRs),
+//   - runs PV of sub-tile s (one assembly block: O stays in the accumulation registers),
+//   - runs the softmax of sub-tile s+1 and dequantizes sub-tile s+2.
+// The index loads and gathers are issued as inline assembly that writes LDS directly; the only
+// waits on them are the explicit vmcnt waits at the top of each iteration, whose counts follow
+// the issue order (loads complete in order).
+
+#include "mla_device.h"
+#include "mla_internal.h"
+
+namespace mla {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kGroupHeads = 32 * kWaves;
+// bf16 tile: token row r at r * 1024 bytes; its 16-byte chunk c (dims 8c .. 8c+7) is stored at
+// chunk position c ^ tile_swizzle(r). The swizzle keeps every access pattern of the kernel free of
+// LDS bank conflicts: 16 rows at one chunk (K row reads, dequant writes) hit 16 different 4-bank
+// groups, and so do 4 rows x 4 consecutive chunks (the transposed V reads).
+constexpr int kTileStride = 1024;
+constexpr int kTileBytes = kSubTokens * kTileStride;    // 32768
+constexpr int kRawBytes = kFp8Chunks * kSubTokens * 16; // 16896, chunk-major [chunk][token][16 B]
+constexpr int kIdxBytes = kSubTokens * 4;     // one index slot (lanes 0..31 write it)
+constexpr int kStages = 3;
+constexpr int kOffRaw = kStages * kTileBytes;
+constexpr int kOffIdx = kOffRaw + kStages * kRawBytes;
+constexpr int kOffFlags = kOffIdx + kWaves * kStages * kIdxBytes;
+constexpr int kLdsBytes = kOffFlags + 16;
+// Largest allowed excess of a score over its head's probability reference, in log2 units: P stays
+// below 2^64, the sums far inside fp32 range for any cache value in the exactly decodable range.
+constexpr float kRefSlack = 64.0f;
+
+// Gather instructions per wave and sub-tile: fp8 = 4 chunk pairs + 1 scale chunk instruction,
+// fp4 = 2 chunk pairs + 1 scale chunk instruction.
+constexpr int kGatherFp8 = 5;
+constexpr int kGatherFp4 = 3;
+
+__device__ __forceinline__ int lane_id() {
+  int l = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  asm volatile("" : "+v"(l));
+  return l;
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// 16-byte and 4-byte global -> LDS copies: the wave's active lanes write LDS bytes m0 + 16 * lane
+// (resp. m0 + 4 * lane). m0 is saved and restored; `lds_base` must be wave-uniform. The masked
+// forms run the copy with EXEC = `lanes` (wave-uniform, never 0) and restore EXEC afterwards, so
+// that a partial-wave copy needs no branch around it.
+__device__ __forceinline__ void copy16_to_lds(const void* gptr, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_base), "v"(gptr)
+      : "memory");
+}
+// Same copy from gptr + OFF: the instruction's immediate offset applies to the LDS address as well
+// (LDS address = m0 + offset + 16 * lane), so m0 is set to lds_base - OFF.
+template <int OFF>
+__device__ __forceinline__ void copy16_to_lds_off(const void* gptr, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, off offset:%3\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_base - OFF), "v"(gptr), "i"(OFF)
+      : "memory");
+}
+__device__ __forceinline__ void copy16_to_lds_masked(const void* gptr, uint32_t lds_base, uint64_t lanes) {
+  uint32_t saved;
+  uint64_t saved_exec;
+  asm volatile(
+      "s_mov_b64 %1, exec\n\t"
+      "s_mov_b64 exec, %4\n\t"
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %3, off\n\t"
+      "s_mov_b32 m0, %0\n\t"
+      "s_mov_b64 exec, %1"
+      : "=&s"(saved), "=&s"(saved_exec)
+      : "s"(lds_base), "v"(gptr), "s"(lanes)
+      : "memory");
+}
+__device__ __forceinline__ void copy4_to_lds_masked(const void* gptr, uint32_t lds_base, uint64_t lanes) {
+  uint32_t saved;
+  uint64_t saved_exec;
+  asm volatile(
+      "s_mov_b64 %1, exec\n\t"
+      "s_mov_b64 exec, %4\n\t"
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %3, off\n\t"
+      "s_mov_b32 m0, %0\n\t"
+      "s_mov_b64 exec, %1"
+      : "=&s"(saved), "=&s"(saved_exec)
+      : "s"(lds_base), "v"(gptr), "s"(lanes)
+      : "memory");
+}
+
+// One MFMA step as an assembly statement: QK^T (scores in VGPRs, chained) and PV (O in the
+// accumulation registers). Used where other work is interleaved between the steps.
+__device__ __forceinline__ void mfma_qk_first(f32x16& s, const bf16x8& k, const bf16x8& q) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(s) : "v"(k), "v"(q));
+}
+__device__ __forceinline__ void mfma_qk(f32x16& s, const bf16x8& k, const bf16x8& q) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(k), "v"(q));
+}
+__device__ __forceinline__ void mfma_pv(f32x16& o, const bf16x8& v, const bf16x8& pb) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(o) : "v"(v), "v"(pb));
+}
+
+typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+__device__ __forceinline__ bf16x8 lds_k(uint32_t a) {
+  return __builtin_bit_cast(bf16x8, *(lds_u32x4*)(uintptr_t)a);
+}
+__device__ __forceinline__ bf16x8 lds_v(uint32_t a0, uint32_t a1) {
+  const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(uintptr_t)a0);
+  const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(uintptr_t)a1);
+  return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// 8 e4m3 values (two words) -> bf16 with an e8m0 scale (see dequant_fp8_16).
+__device__ __forceinline__ bf16x8 dequant_fp8_8(uint32_t w0, uint32_t w1, uint32_t scale_byte) {
+  const float s = __builtin_bit_cast(float, scale_byte << 23);
+  return cat4(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, s, false),
+              __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, s, true),
+              __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, s, false),
+              __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, s, true));
+}
+
+// Wait until at most n of this wave's vector memory operations are outstanding (and all of its
+// LDS operations are done), then synchronise the workgroup. n is wave-uniform.
+__device__ __forceinline__ void wait_and_barrier(int n) {
+  switch (n) {
+    case 0: asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
+    case 1: asm volatile("s_waitcnt vmcnt(1) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
+    case 3: asm volatile("s_waitcnt vmcnt(3) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
+    case 4: asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
+    case 5: asm volatile("s_waitcnt vmcnt(5) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
+    case 6: asm volatile("s_waitcnt vmcnt(6) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
+  }
+}
+
+__device__ __forceinline__ int tile_swizzle(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
+__device__ __forceinline__ u32x4 lds_read16(const char* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ void lds_write16(char* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+
+// Where sub-tile j of a row segment starting at unit t0 lives in the index arrays.
+struct SubTile {
+  bool fp4;
+  int pos0;       // position of token 0 of the sub-tile inside its index row
+  int count;      // index entries of that row (topk or extra_topk)
+};
+
+template <bool EXTRA>
+__device__ __forceinline__ SubTile locate(const DecodeParams& p, int t0, int j) {
+  const int unit = t0 + (j >> 1);
+  SubTile st;
+  st.fp4 = EXTRA && unit >= p.tiles_k;
+  const int u = st.fp4 ? unit - p.tiles_k : unit;
+  st.pos0 = u * kUnitTokens + (j & 1) * kSubTokens;
+  st.count = st.fp4 ? p.extra_topk : p.topk;
+  return st;
+}
+
+
+// QK^T of one sub-tile: S^T[32 tokens x 32 heads] = K[32 x 512] Q^T with 32 chained
+// v_mfma_f32_32x32x16_bf16 steps. Step kk reads this lane's K fragment (token l%32, dims
+// 16kk + 8(l/32) .. +7) at a[kk % 8] + 256 (kk / 8) (swizzled tile, see tile_swizzle). K fragments
+// are read four steps ahead into eight rotating registers, so no fragment is overwritten while an
+// MFMA that reads it may still be in flight.
+//
+// Written as one assembly block so that the scores land in VGPRs: with O occupying all 256
+// accumulation registers, compiler-selected MFMAs would put the scores there as well. The block
+// waits for its own LDS reads (lgkmcnt, after draining any earlier LDS/scalar operations), starts
+// with 5 wait states (Q may have just been moved by VALU instructions) and ends with 20, more than
+// the 12 the compiler inserts between this MFMA writing a VGPR and a VALU reading it.
+__device__ __forceinline__ f32x16 qk_chain(const uint32_t (&a)[8], const bf16x8 (&q)[32]) {
+  f32x16 s;
+  bf16x8 k0, k1, k2, k3, k4, k5, k6, k7;
+  asm volatile(
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "s_nop 4\n\t"
+      "ds_read_b128 %[k0], %[a0] offset:0\n\t"
+      "ds_read_b128 %[k1], %[a1] offset:0\n\t"
+      "ds_read_b128 %[k2], %[a2] offset:0\n\t"
+      "ds_read_b128 %[k3], %[a3] offset:0\n\t"
+      "s_waitcnt lgkmcnt(3)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[k0], %[q0], 0\n\t"
+      "ds_read_b128 %[k4], %[a4] offset:0\n\t"
+      "s_waitcnt lgkmcnt(3)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[k1], %[q1], %[s]\n\t"
+      "ds_read_b128 %[k5], %[a5] offset:0\n\t"
+      "s_waitcnt lgkmcnt(3)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[k2], %[q2], %[s]\n\t"
+      "ds_read_b128 %[k6], %[a6] offset:0\n\t"
+      "s_waitcnt lgkmcnt(3)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[k3], %[q3], %[s]\n\t"
+      "ds_read_b128 %[k7], %[a7] offset:0\n\t"
+      "s_waitcnt lgkmcnt(3)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[k4], %[q4], %[s]\n\t"
+      "ds_read_b128 %[k0], %[a0] offset:256\n\t"
+      "s_waitcnt lgkmcnt(3)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[k5], %[q5], %[s]\n\t"
+      "ds_read_b128 %[k1], %[a1] offset:256\n\t"
+      "s_waitcnt lgkmcnt(3)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[k6], %[q6], %[s]\n\t"
+      "ds_read_b128 %[k2], %[a2] offset:256\n\t"
+      "s_waitcnt lgkmcnt(3)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[k7], %[q7], %[s]\n\t"
+      "ds_read_b128 %[k3], %[a3] offset:256\n\t"
+      "s_waitcnt lgkmcnt(3)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[k0], %[q8], %[s]\n\t"
+      "ds_read_b128 %[k4], %[a4] offset:256\n\t"
+      "s_waitcnt lgkmcnt(3)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[k1], %[q9], %[s]\n\t"
+      "ds_read_b128 %[k5], %[a5] offset:256\n\t"
+      "s_waitcnt lgkmcnt(3)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[k2], %[q10], %[s]\n\t"
+      "ds_read_b128 %[k6], %[a6] offset:256\n\t"
+      "s_waitcnt lgkmcnt(3)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[k3], %[q11], %[s]\n\t"
+      "ds_read_b128 %[k7], %[a7] offset:256\n\t"
+      "s_waitcnt lgkmcnt(3)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[k4], %[q12], %[s]\n\t"
+      "ds_read_b128 %[k0], %[a0] offset:512\n\t"
+      "s_waitcnt lgkmcnt(3)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[k5], %[q13], %[s]\n\t"
+      "ds_read_b128 %[k1], %[a1] offset:512\n\t"
+      "s_waitcnt lgkmcnt(3)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[k6], %[q14], %[s]\n\t"
+      "ds_read_b128 %[k2], %[a2] offset:512\n\t"
+      "s_waitcnt lgkmcnt(3)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[k7], %[q15], %[s]\n\t"
+      "ds_read_b128 %[k3], %[a3] offset:512\n\t"
+      "s_waitcnt lgkmcnt(3)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[k0], %[q16], %[s]\n\t"
+      "ds_read_b128 %[k4], %[a4] offset:512\n\t"
+      "s_waitcnt lgkmcnt(3)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[k1], %[q17], %[s]\n\t"
+      "ds_read_b128 %[k5], %[a5] offset:512\n\t"
+      "s_waitcnt lgkmcnt(3)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[k2], %[q18], %[s]\n\t"
+      "ds_read_b128 %[k6], %[a6] offset:512\n\t"
+      "s_waitcnt lgkmcnt(3)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[k3], %[q19], %[s]\n\t"
+      "ds_read_b128 %[k7], %[a7] offset:512\n\t"
+      "s_waitcnt lgkmcnt(3)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[k4], %[q20], %[s]\n\t"
+      "ds_read_b128 %[k0], %[a0] offset:768\n\t"
+      "s_waitcnt lgkmcnt(3)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[k5], %[q21], %[s]\n\t"
+      "ds_read_b128 %[k1], %[a1] offset:768\n\t"
+      "s_waitcnt lgkmcnt(3)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[k6], %[q22], %[s]\n\t"
+      "ds_read_b128 %[k2], %[a2] offset:768\n\t"
+      "s_waitcnt lgkmcnt(3)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[k7], %[q23], %[s]\n\t"
+      "ds_read_b128 %[k3], %[a3] offset:768\n\t"
+      "s_waitcnt lgkmcnt(3)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[k0], %[q24], %[s]\n\t"
+      "ds_read_b128 %[k4], %[a4] offset:768\n\t"
+      "s_waitcnt lgkmcnt(3)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[k1], %[q25], %[s]\n\t"
+      "ds_read_b128 %[k5], %[a5] offset:768\n\t"
+      "s_waitcnt lgkmcnt(3)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[k2], %[q26], %[s]\n\t"
+      "ds_read_b128 %[k6], %[a6] offset:768\n\t"
+      "s_waitcnt lgkmcnt(3)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[k3], %[q27], %[s]\n\t"
+      "ds_read_b128 %[k7], %[a7] offset:768\n\t"
+      "s_waitcnt lgkmcnt(3)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[k4], %[q28], %[s]\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[k5], %[q29], %[s]\n\t"
+      "s_waitcnt lgkmcnt(1)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[k6], %[q30], %[s]\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[s], %[k7], %[q31], %[s]\n\t"
+      "s_nop 15\n\t"
+      "s_nop 3"
+      : [s] "=&v"(s), [k0] "=&v"(k0), [k1] "=&v"(k1), [k2] "=&v"(k2), [k3] "=&v"(k3), [k4] "=&v"(k4), [k5] "=&v"(k5), [k6] "=&v"(k6), [k7] "=&v"(k7)
+      : [a0] "v"(a[0]), [a1] "v"(a[1]), [a2] "v"(a[2]), [a3] "v"(a[3]), [a4] "v"(a[4]), [a5] "v"(a[5]), [a6] "v"(a[6]), [a7] "v"(a[7]), [q0] "v"(q[0]), [q1] "v"(q[1]), [q2] "v"(q[2]), [q3] "v"(q[3]), [q4] "v"(q[4]), [q5] "v"(q[5]), [q6] "v"(q[6]), [q7] "v"(q[7]), [q8] "v"(q[8]), [q9] "v"(q[9]), [q10] "v"(q[10]), [q11] "v"(q[11]), [q12] "v"(q[12]), [q13] "v"(q[13]), [q14] "v"(q[14]), [q15] "v"(q[15]), [q16] "v"(q[16]), [q17] "v"(q[17]), [q18] "v"(q[18]), [q19] "v"(q[19]), [q20] "v"(q[20]), [q21] "v"(q[21]), [q22] "v"(q[22]), [q23] "v"(q[23]), [q24] "v"(q[24]), [q25] "v"(q[25]), [q26] "v"(q[26]), [q27] "v"(q[27]), [q28] "v"(q[28]), [q29] "v"(q[29]), [q30] "v"(q[30]), [q31] "v"(q[31])
+      : "memory");
+  return s;
+}
+
+
+// PV of one sub-tile: O^T[512 dims x 32 heads] += V^T P^T as 32 v_mfma_f32_32x32x16_bf16 steps
+// (step i: token half ks = i / 16, dim block d = i % 16). The V^T operand of a step is two
+// transposed LDS reads (ds_read_b64_tr_b16) at a[d % 4] and a[4 + d % 4], plus 16384 ks +
+// 256 (d / 4) (swizzled tile, see tile_swizzle). Reads run three steps ahead through six fixed operand buffers
+// (v232..v255, declared clobbered so that the compiler keeps nothing there); O stays in the
+// accumulation registers. The block starts with 5 wait states (P may have just been written by
+// VALU instructions) and ends with 20 (before O is read outside).
+__device__ __forceinline__ void pv_chain(const uint32_t (&a)[8], f32x16 (&o)[16], const bf16x8 (&pb)[2]) {
+  asm volatile(
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "s_nop 4\n\t"
+      "ds_read_b64_tr_b16 v[232:233], %[v0] offset:0\n\t"
+      "ds_read_b64_tr_b16 v[234:235], %[v4] offset:0\n\t"
+      "ds_read_b64_tr_b16 v[236:237], %[v1] offset:0\n\t"
+      "ds_read_b64_tr_b16 v[238:239], %[v5] offset:0\n\t"
+      "ds_read_b64_tr_b16 v[240:241], %[v2] offset:0\n\t"
+      "ds_read_b64_tr_b16 v[242:243], %[v6] offset:0\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[o0], v[232:235], %[p0], %[o0]\n\t"
+      "ds_read_b64_tr_b16 v[244:245], %[v3] offset:0\n\t"
+      "ds_read_b64_tr_b16 v[246:247], %[v7] offset:0\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[o1], v[236:239], %[p0], %[o1]\n\t"
+      "ds_read_b64_tr_b16 v[248:249], %[v0] offset:256\n\t"
+      "ds_read_b64_tr_b16 v[250:251], %[v4] offset:256\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[o2], v[240:243], %[p0], %[o2]\n\t"
+      "ds_read_b64_tr_b16 v[252:253], %[v1] offset:256\n\t"
+      "ds_read_b64_tr_b16 v[254:255], %[v5] offset:256\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[o3], v[244:247], %[p0], %[o3]\n\t"
+      "ds_read_b64_tr_b16 v[232:233], %[v2] offset:256\n\t"
+      "ds_read_b64_tr_b16 v[234:235], %[v6] offset:256\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[o4], v[248:251], %[p0], %[o4]\n\t"
+      "ds_read_b64_tr_b16 v[236:237], %[v3] offset:256\n\t"
+      "ds_read_b64_tr_b16 v[238:239], %[v7] offset:256\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[o5], v[252:255], %[p0], %[o5]\n\t"
+      "ds_read_b64_tr_b16 v[240:241], %[v0] offset:512\n\t"
+      "ds_read_b64_tr_b16 v[242:243], %[v4] offset:512\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[o6], v[232:235], %[p0], %[o6]\n\t"
+      "ds_read_b64_tr_b16 v[244:245], %[v1] offset:512\n\t"
+      "ds_read_b64_tr_b16 v[246:247], %[v5] offset:512\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[o7], v[236:239], %[p0], %[o7]\n\t"
+      "ds_read_b64_tr_b16 v[248:249], %[v2] offset:512\n\t"
+      "ds_read_b64_tr_b16 v[250:251], %[v6] offset:512\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[o8], v[240:243], %[p0], %[o8]\n\t"
+      "ds_read_b64_tr_b16 v[252:253], %[v3] offset:512\n\t"
+      "ds_read_b64_tr_b16 v[254:255], %[v7] offset:512\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[o9], v[244:247], %[p0], %[o9]\n\t"
+      "ds_read_b64_tr_b16 v[232:233], %[v0] offset:768\n\t"
+      "ds_read_b64_tr_b16 v[234:235], %[v4] offset:768\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[o10], v[248:251], %[p0], %[o10]\n\t"
+      "ds_read_b64_tr_b16 v[236:237], %[v1] offset:768\n\t"
+      "ds_read_b64_tr_b16 v[238:239], %[v5] offset:768\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[o11], v[252:255], %[p0], %[o11]\n\t"
+      "ds_read_b64_tr_b16 v[240:241], %[v2] offset:768\n\t"
+      "ds_read_b64_tr_b16 v[242:243], %[v6] offset:768\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[o12], v[232:235], %[p0], %[o12]\n\t"
+      "ds_read_b64_tr_b16 v[244:245], %[v3] offset:768\n\t"
+      "ds_read_b64_tr_b16 v[246:247], %[v7] offset:768\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[o13], v[236:239], %[p0], %[o13]\n\t"
+      "ds_read_b64_tr_b16 v[248:249], %[v0] offset:16384\n\t"
+      "ds_read_b64_tr_b16 v[250:251], %[v4] offset:16384\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[o14], v[240:243], %[p0], %[o14]\n\t"
+      "ds_read_b64_tr_b16 v[252:253], %[v1] offset:16384\n\t"
+      "ds_read_b64_tr_b16 v[254:255], %[v5] offset:16384\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[o15], v[244:247], %[p0], %[o15]\n\t"
+      "ds_read_b64_tr_b16 v[232:233], %[v2] offset:16384\n\t"
+      "ds_read_b64_tr_b16 v[234:235], %[v6] offset:16384\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[o0], v[248:251], %[p1], %[o0]\n\t"
+      "ds_read_b64_tr_b16 v[236:237], %[v3] offset:16384\n\t"
+      "ds_read_b64_tr_b16 v[238:239], %[v7] offset:16384\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[o1], v[252:255], %[p1], %[o1]\n\t"
+      "ds_read_b64_tr_b16 v[240:241], %[v0] offset:16640\n\t"
+      "ds_read_b64_tr_b16 v[242:243], %[v4] offset:16640\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[o2], v[232:235], %[p1], %[o2]\n\t"
+      "ds_read_b64_tr_b16 v[244:245], %[v1] offset:16640\n\t"
+      "ds_read_b64_tr_b16 v[246:247], %[v5] offset:16640\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[o3], v[236:239], %[p1], %[o3]\n\t"
+      "ds_read_b64_tr_b16 v[248:249], %[v2] offset:16640\n\t"
+      "ds_read_b64_tr_b16 v[250:251], %[v6] offset:16640\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[o4], v[240:243], %[p1], %[o4]\n\t"
+      "ds_read_b64_tr_b16 v[252:253], %[v3] offset:16640\n\t"
+      "ds_read_b64_tr_b16 v[254:255], %[v7] offset:16640\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[o5], v[244:247], %[p1], %[o5]\n\t"
+      "ds_read_b64_tr_b16 v[232:233], %[v0] offset:16896\n\t"
+      "ds_read_b64_tr_b16 v[234:235], %[v4] offset:16896\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[o6], v[248:251], %[p1], %[o6]\n\t"
+      "ds_read_b64_tr_b16 v[236:237], %[v1] offset:16896\n\t"
+      "ds_read_b64_tr_b16 v[238:239], %[v5] offset:16896\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[o7], v[252:255], %[p1], %[o7]\n\t"
+      "ds_read_b64_tr_b16 v[240:241], %[v2] offset:16896\n\t"
+      "ds_read_b64_tr_b16 v[242:243], %[v6] offset:16896\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[o8], v[232:235], %[p1], %[o8]\n\t"
+      "ds_read_b64_tr_b16 v[244:245], %[v3] offset:16896\n\t"
+      "ds_read_b64_tr_b16 v[246:247], %[v7] offset:16896\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[o9], v[236:239], %[p1], %[o9]\n\t"
+      "ds_read_b64_tr_b16 v[248:249], %[v0] offset:17152\n\t"
+      "ds_read_b64_tr_b16 v[250:251], %[v4] offset:17152\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[o10], v[240:243], %[p1], %[o10]\n\t"
+      "ds_read_b64_tr_b16 v[252:253], %[v1] offset:17152\n\t"
+      "ds_read_b64_tr_b16 v[254:255], %[v5] offset:17152\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[o11], v[244:247], %[p1], %[o11]\n\t"
+      "ds_read_b64_tr_b16 v[232:233], %[v2] offset:17152\n\t"
+      "ds_read_b64_tr_b16 v[234:235], %[v6] offset:17152\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[o12], v[248:251], %[p1], %[o12]\n\t"
+      "ds_read_b64_tr_b16 v[236:237], %[v3] offset:17152\n\t"
+      "ds_read_b64_tr_b16 v[238:239], %[v7] offset:17152\n\t"
+      "s_waitcnt lgkmcnt(4)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[o13], v[252:255], %[p1], %[o13]\n\t"
+      "s_waitcnt lgkmcnt(2)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[o14], v[232:235], %[p1], %[o14]\n\t"
+      "s_waitcnt lgkmcnt(0)\n\t"
+      "v_mfma_f32_32x32x16_bf16 %[o15], v[236:239], %[p1], %[o15]\n\t"
+      "s_nop 15\n\t"
+      "s_nop 3"
+      : [o0] "+a"(o[0]), [o1] "+a"(o[1]), [o2] "+a"(o[2]), [o3] "+a"(o[3]), [o4] "+a"(o[4]), [o5] "+a"(o[5]), [o6] "+a"(o[6]), [o7] "+a"(o[7]), [o8] "+a"(o[8]), [o9] "+a"(o[9]), [o10] "+a"(o[10]), [o11] "+a"(o[11]), [o12] "+a"(o[12]), [o13] "+a"(o[13]), [o14] "+a"(o[14]), [o15] "+a"(o[15])
+      : [v0] "v"(a[0]), [v1] "v"(a[1]), [v2] "v"(a[2]), [v3] "v"(a[3]), [v4] "v"(a[4]), [v5] "v"(a[5]), [v6] "v"(a[6]), [v7] "v"(a[7]), [p0] "v"(pb[0]), [p1] "v"(pb[1])
+      : "memory", "v232", "v233", "v234", "v235", "v236", "v237", "v238", "v239", "v240", "v241", "v242", "v243", "v244", "v245", "v246", "v247", "v248", "v249", "v250", "v251", "v252", "v253", "v254", "v255");
+}
+
+template <bool EXTRA>
+__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void sparse_decode_wide_kernel(DecodeParams p) {
+  __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
+  char* const tiles = smem;
+  char* const raws = smem + kOffRaw;
+  int* const redo_flags = reinterpret_cast<int*>(smem + kOffFlags);
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int head_base = blockIdx.y * kGroupHeads + 32 * wave;   // this wave's first head
+  char* const idx_ring = smem + kOffIdx + wave * kStages * kIdxBytes;
+  // lanes of the scale-chunk copies: tokens 8w .. 8w+7 (first lane half; fp4: both halves)
+  const uint64_t scale_lanes_fp8 = 0xFFull << (8 * wave);
+  const uint64_t scale_lanes_fp4 = scale_lanes_fp8 | (scale_lanes_fp8 << 32);
+
+  if constexpr (!EXTRA) {
+    // The fp8 pipeline's first iterations read tile slots no sub-tile has been written to yet
+    // (with zero probabilities); zeros keep those products finite.
+    for (int o = threadIdx.x * 16; o < kStages * kTileBytes; o += 64 * kWaves * 16)
+      lds_write16(tiles + o, u32x4{});
+    __syncthreads();
+  }
+
+  const int32_t* sc = p.sched + blockIdx.x * 8;
+  int row = sc[0];
+  int t0 = sc[1];
+  const int end_row = sc[2];
+  const int end_tile = sc[3];
+  const int slot_first = sc[4];
+  bool first_seg = true;
+
+  while (row < end_row || (row == end_row && t0 < end_tile)) {
+    const int t1 = row < end_row ? p.tiles : end_tile;
+    const int nsub = 2 * (t1 - t0);
+    const int split_base = p.split_ptr[row];
+    const int nsplit = p.split_ptr[row + 1] - split_base;
+    const int slot = first_seg ? slot_first : split_base;
+
+    // ---- Q of this wave's 32 heads, B-operand layout of v_mfma_f32_32x32x16_bf16:
+    // lane l holds head l%32, dims 16kk + 8(l/32) .. +7 of k-step kk. Heads past h_q load a copy
+    // of the last head; their results are never stored.
+    bf16x8 qreg[32];
+    {
+      const int lane = lane_id();
+      const int qh = min(head_base + (lane & 31), p.h_q - 1);
+      const u32x4* qp = reinterpret_cast<const u32x4*>(
+          p.q + ((int64_t)row * p.h_q + qh) * kHeadDim + 8 * (lane >> 5));
+#pragma unroll
+      for (int kk = 0; kk < 32; ++kk) qreg[kk] = __builtin_bit_cast(bf16x8, qp[2 * kk]);
+    }
+    // Q is resident before any asynchronous copy of this segment is issued, so the compiler's
+    // own wait for it cannot end up waiting for the gathers as well.
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+
+    // ---- asynchronous stages (see the file comment).
+    // Index load of sub-tile j into this wave's index slot j % 3 (lanes 0..31, one entry each;
+    // entries past the end of the index row are fetched from a clamped address and replaced by
+    // -1 when read). It is issued for every iteration: past the last sub-tile, or for a selection
+    // of size 0 (no index array), it reads from the schedule instead (a valid address).
+    auto load_indices = [&](int j) {
+      const int lane = lane_id();
+      const int32_t* src_ptr = p.sched;
+      if (j < nsub) {
+        const SubTile st = locate<EXTRA>(p, t0, j);
+        if (st.count > 0)
+          src_ptr = (st.fp4 ? p.xidx : p.idx) + (int64_t)row * st.count + min(st.pos0 + lane, st.count - 1);
+      }
+      copy4_to_lds_masked(src_ptr, __builtin_amdgcn_readfirstlane(lds_addr(idx_ring + (j % 3) * kIdxBytes)),
+                          0xFFFFFFFFull);
+    };
+    // Gather of sub-tile j into raw slot j % 3; returns the validity mask of its 32 tokens.
+    // Ignored tokens fetch record 0 (it exists whenever the selection is not empty), so every wave
+    // issues a fixed number of copies per sub-tile; their values are never used. A sub-tile of an
+    // empty selection issues nothing.
+    auto gather = [&](int j) -> uint32_t {
+      const SubTile st = locate<EXTRA>(p, t0, j);
+      if (st.count == 0) return 0u;
+      const int lane = lane_id();
+      const int t = lane & 31;
+      const int hh = lane >> 5;
+      const int v = *reinterpret_cast<const int*>(idx_ring + (j % 3) * kIdxBytes + 4 * t);
+      const bool valid = st.pos0 + t < st.count && v >= 0;
+      const uint32_t mask = (uint32_t)__ballot(valid);
+      const int tok = valid ? v : 0;
+      char* raw = raws + (j % 3) * kRawBytes;
+      const uint32_t raw_lds = __builtin_amdgcn_readfirstlane(lds_addr(raw));
+      if (!st.fp4) {
+        const uint8_t* rec = p.kc + (int64_t)tok * kFp8Rec;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int q = wave + 4 * i;                       // chunks 2q (hh = 0) and 2q + 1
+          copy16_to_lds(rec + (2 * q + hh) * 16, __builtin_amdgcn_readfirstlane(raw_lds + 1024 * q));
+        }
+        copy16_to_lds_masked(rec + 512, __builtin_amdgcn_readfirstlane(raw_lds + 32 * 512), scale_lanes_fp8);
+      } else {
+        const uint8_t* rec = p.xc + (int64_t)tok * kFp4Rec;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int q = wave + 4 * i;
+          copy16_to_lds(rec + (2 * q + hh) * 16, __builtin_amdgcn_readfirstlane(raw_lds + 1024 * q));
+        }
+        copy16_to_lds_masked(rec + (16 + hh) * 16, __builtin_amdgcn_readfirstlane(raw_lds + 16 * 512),
+                             scale_lanes_fp4);
+      }
+      return mask;
+    };
+    // Dequantization of sub-tile j: this wave's 128 dims of all 32 tokens, raw slot -> bf16 tile
+    // slot j % 3 (ignored tokens become zeros).
+    auto dequant = [&](int j, uint32_t mask) {
+      const SubTile st = locate<EXTRA>(p, t0, j);
+      const int lane = lane_id();
+      const int t = lane & 31;
+      const int g = lane >> 5;
+      const bool valid = (mask >> t) & 1u;
+      const char* raw = raws + (j % 3) * kRawBytes;
+      char* trow = tiles + (j % 3) * kTileBytes + t * kTileStride;
+      const int sw = tile_swizzle(t);
+      auto chunk = [&](int c) { return trow + 16 * (c ^ sw); };   // bf16 chunk c of this token
+      if (!st.fp4) {
+        const int c0 = 8 * wave + 4 * g;                     // first of this lane's 4 fp8 chunks
+        const uint32_t sc2 = *reinterpret_cast<const uint16_t*>(raw + (32 * kSubTokens + t) * 16 + c0 / 2);
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) {
+          const u32x4 r = lds_read16(raw + ((c0 + cc) * kSubTokens + t) * 16);
+          bf16x8 lo, hi;
+          dequant_fp8_16(r, (sc2 >> (8 * (cc >> 1))) & 0xFFu, lo, hi);
+          lds_write16(chunk(2 * (c0 + cc)), valid ? __builtin_bit_cast(u32x4, lo) : u32x4{});
+          lds_write16(chunk(2 * (c0 + cc) + 1), valid ? __builtin_bit_cast(u32x4, hi) : u32x4{});
+        }
+      } else {
+        const int c0 = 4 * wave + 2 * g;                     // 2 data chunks = dims 32c0 .. 32c0+63
+        const int j0 = 8 * wave + 4 * g;                     // e4m3 scales j0 .. j0+3
+        const uint32_t sc4 = *reinterpret_cast<const uint32_t*>(
+            raw + ((16 + (j0 >> 4)) * kSubTokens + t) * 16 + (j0 & 15));
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) {
+          const u32x4 r = lds_read16(raw + ((c0 + cc) * kSubTokens + t) * 16);
+          bf16x8 a0, a1, a2, a3;
+          dequant_fp4_16(r[0], r[1], e4m3_to_f32(sc4 >> (16 * cc)), a0, a1);
+          dequant_fp4_16(r[2], r[3], e4m3_to_f32(sc4 >> (16 * cc + 8)), a2, a3);
+          const int b = 4 * (c0 + cc);                       // bf16 chunks b .. b+3
+          lds_write16(chunk(b), valid ? __builtin_bit_cast(u32x4, a0) : u32x4{});
+          lds_write16(chunk(b + 1), valid ? __builtin_bit_cast(u32x4, a1) : u32x4{});
+          lds_write16(chunk(b + 2), valid ? __builtin_bit_cast(u32x4, a2) : u32x4{});
+          lds_write16(chunk(b + 3), valid ? __builtin_bit_cast(u32x4, a3) : u32x4{});
+        }
+      }
+    };
+    auto gather_count = [&](int j) -> int {
+      if (j < 0 || j >= nsub) return 0;
+      const SubTile st = locate<EXTRA>(p, t0, j);
+      return st.count == 0 ? 0 : st.fp4 ? kGatherFp4 : kGatherFp8;
+    };
+    auto is_fp8 = [&](int j) -> bool { return !locate<EXTRA>(p, t0, j).fp4; };
+
+    // Per-lane LDS addresses in tile slot 0 (add slot * kTileBytes).
+    // QK^T step kk reads token row l%32, logical chunk 2kk + l/32: with s = tile_swizzle(row) that is
+    // physical chunk 2(kk ^ (s >> 1)) + ((l/32) ^ (s & 1)), i.e. k_addr[kk % 8] + 256 (kk / 8).
+    // PV step (ks, d) reads, for h = 0, 1, token row 16ks + 8((l/16)/2) + 4h + (l%16)/4 and logical
+    // chunk 4d + 2((l/16)%2) + (l%4)/2 (8-byte half l%2), i.e. v_addr[4h + d%4] + 16384 ks +
+    // 256 (d / 4).
+    uint32_t k_addr[8], v_addr[8];
+    {
+      const int lane = lane_id();
+      const int r = lane & 31, g = lane >> 5, s = tile_swizzle(r);
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        k_addr[j] = lds_addr(tiles + r * kTileStride + 32 * (j ^ (s >> 1)) + 16 * (g ^ (s & 1)));
+      const int g2 = lane >> 4, jj = lane & 15;
+      const int c_lo = 2 * (g2 & 1) + ((jj & 3) >> 1);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int rw = 8 * (g2 >> 1) + 4 * h + (jj >> 2);
+        const int sr = tile_swizzle(rw);
+#pragma unroll
+        for (int dd = 0; dd < 4; ++dd)
+          v_addr[4 * h + dd] = lds_addr(tiles + rw * kTileStride + 16 * ((4 * dd + c_lo) ^ sr) + 8 * (jj & 1));
+      }
+    }
+    auto slot_addr = [&](const uint32_t (&base)[8], int sl, uint32_t (&out)[8]) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) out[j] = base[j] + sl * kTileBytes;
+    };
+
+    // ---- softmax state. Scores are in log2 units (x = q.k * scale * log2 e). Probabilities are
+    // taken against a fixed per-head reference m_ref, the maximum of the head's first sub-tile with
+    // a valid token, instead of a running maximum: O is never rescaled inside the loop. m_max
+    // tracks the true maximum. If it ends more than kRefSlack above m_ref for some head (larger
+    // probabilities could overflow), the segment is computed again with m_ref = m_max, which is
+    // then exact; for scores of realistic range that second pass never runs.
+    float m_ref_next = -__builtin_inff();     // reference for the next pass (-inf: take the first)
+    f32x16 oacc[16];
+    float m_ref, m_max, l_sum;
+    for (int pass = 0;; ++pass) {
+      m_ref = m_ref_next;
+      m_max = -__builtin_inff();
+      l_sum = 0.0f;
+      {
+        // 0 x 0 + 0 per block, in one assembly block whose leading wait states separate the VALU
+        // write of the zero operand from its first read by an MFMA (an MFMA issued right after that
+        // write reads stale lanes). The O accumulators then only ever take values from assembly
+        // with AGPR constraints, so the compiler never moves them through VGPRs.
+        const bf16x8 zero8 = bf16x8{};
+        asm volatile(
+            "s_nop 4\n\t"
+            "v_mfma_f32_32x32x16_bf16 %0, %16, %16, 0\n\t"
+            "v_mfma_f32_32x32x16_bf16 %1, %16, %16, 0\n\t"
+            "v_mfma_f32_32x32x16_bf16 %2, %16, %16, 0\n\t"
+            "v_mfma_f32_32x32x16_bf16 %3, %16, %16, 0\n\t"
+            "v_mfma_f32_32x32x16_bf16 %4, %16, %16, 0\n\t"
+            "v_mfma_f32_32x32x16_bf16 %5, %16, %16, 0\n\t"
+            "v_mfma_f32_32x32x16_bf16 %6, %16, %16, 0\n\t"
+            "v_mfma_f32_32x32x16_bf16 %7, %16, %16, 0\n\t"
+            "v_mfma_f32_32x32x16_bf16 %8, %16, %16, 0\n\t"
+            "v_mfma_f32_32x32x16_bf16 %9, %16, %16, 0\n\t"
+            "v_mfma_f32_32x32x16_bf16 %10, %16, %16, 0\n\t"
+            "v_mfma_f32_32x32x16_bf16 %11, %16, %16, 0\n\t"
+            "v_mfma_f32_32x32x16_bf16 %12, %16, %16, 0\n\t"
+            "v_mfma_f32_32x32x16_bf16 %13, %16, %16, 0\n\t"
+            "v_mfma_f32_32x32x16_bf16 %14, %16, %16, 0\n\t"
+            "v_mfma_f32_32x32x16_bf16 %15, %16, %16, 0"
+            : "=a"(oacc[0]), "=a"(oacc[1]), "=a"(oacc[2]), "=a"(oacc[3]), "=a"(oacc[4]),
+              "=a"(oacc[5]), "=a"(oacc[6]), "=a"(oacc[7]), "=a"(oacc[8]), "=a"(oacc[9]),
+              "=a"(oacc[10]), "=a"(oacc[11]), "=a"(oacc[12]), "=a"(oacc[13]), "=a"(oacc[14]),
+              "=a"(oacc[15])
+            : "v"(zero8));
+      }
+
+      // Softmax of one sub-tile's scores sv (lane l: head l%32, tokens 8(r/4) + 4(l/32) + r%4 in
+      // sv[r]; lanes l and l^32 together hold the head's 32 tokens), split into steps so that the
+      // pieces can be spread over the PV MFMAs: 0-3 scale and mask 4 scores each, 4 the maximum,
+      // 5-12 two exponentials each, 13-14 the P^T operand of one token half each, 15 the sum.
+      struct SoftmaxTemps { float x[16], e[16], mx, ls; };    // local to one sub-tile's softmax
+      auto softmax_step = [&](SoftmaxTemps& st, int step, const f32x16& sv, uint32_t mask,
+                              bf16x8 (&pb)[2]) {
+        float (&x)[16] = st.x;
+        float (&e)[16] = st.e;
+        float& mx = st.mx;
+        float& ls = st.ls;
+        const int lane = lane_id();
+        if (step < 4) {
+          if (step == 0) { mx = -__builtin_inff(); ls = 0.0f; }
+#pragma unroll
+          for (int r = 4 * step; r < 4 * step + 4; ++r) x[r] = sv[r] * p.scale_log2;
+          if (mask != 0xFFFFFFFFu) {             // ignored tokens in this sub-tile: -inf scores
+            const uint32_t mq = mask >> (4 * (lane >> 5));
+#pragma unroll
+            for (int r = 4 * step; r < 4 * step + 4; ++r)
+              if (!((mq >> (8 * (r >> 2) + (r & 3))) & 1u)) x[r] = -__builtin_inff();
+          }
+          mx = fmaxf(mx, fmaxf(fmaxf(x[4 * step], x[4 * step + 1]), fmaxf(x[4 * step + 2], x[4 * step + 3])));
+        } else if (step == 4) {
+          mx = max_xor32(mx);             // -inf only if the sub-tile has no valid token
+          m_max = fmaxf(m_max, mx);
+          m_ref = m_ref == -__builtin_inff() ? mx : m_ref;
+          // while no valid token has been seen (m_ref = -inf) every x is -inf: exp2(-inf - 0) = 0
+          mx = m_ref == -__builtin_inff() ? 0.0f : m_ref;   // reused as the exponent offset
+        } else if (step < 13) {
+#pragma unroll
+          for (int r = 2 * (step - 5); r < 2 * (step - 5) + 2; ++r) {
+            e[r] = __builtin_amdgcn_exp2f(x[r] - mx);     // 0 for ignored tokens (x = -inf)
+            ls += e[r];
+          }
+        } else if (step < 15) {
+          // P^T operand for token block ks: lane l needs head l%32 and tokens 16ks + 8(l/32) .. +7.
+          // X (r = 8ks..8ks+3) and Y (r = 8ks+4..8ks+7) hold tokens 16ks + 4g + 0..3 and
+          // 16ks + 8 + 4g + 0..3 (g = l/32); one permlane32 swap of X's upper half with Y's lower
+          // half leaves tokens 16ks + 8g' + 0..3 in X and + 4..7 in Y for lane group g'.
+          const int ks = step - 13;
+          uint32_t xw[2], yw[2];
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            bf16x2 xa, ya;
+            xa[0] = (__bf16)e[8 * ks + 2 * h];
+            xa[1] = (__bf16)e[8 * ks + 2 * h + 1];
+            ya[0] = (__bf16)e[8 * ks + 4 + 2 * h];
+            ya[1] = (__bf16)e[8 * ks + 4 + 2 * h + 1];
+            auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, xa),
+                                                       __builtin_bit_cast(uint32_t, ya), false, false);
+            xw[h] = (uint32_t)sw[0];
+            yw[h] = (uint32_t)sw[1];
+          }
+          const u32x4 packed = {xw[0], xw[1], yw[0], yw[1]};
+          pb[ks] = __builtin_bit_cast(bf16x8, packed);
+        } else if (step == 15) {
+          l_sum += sum_xor32(ls);
+        }
+      };
+      auto softmax = [&](const f32x16& sv, uint32_t mask, bf16x8 (&pb)[2]) {
+        SoftmaxTemps st;
+#pragma unroll
+        for (int step = 0; step < 16; ++step) softmax_step(st, step, sv, mask, pb);
+      };
+
+      // Validity masks of sub-tiles s .. s+4 (scalar ring) and the P^T operand of sub-tile s.
+      uint32_t mk0 = 0, mk1 = 0, mk2 = 0, mk3 = 0, mk4 = 0;
+      bf16x8 pb_cur[2] = {bf16x8{}, bf16x8{}};
+      // opaque, so that no copy of the loop is specialised for this constant
+      asm volatile("" : "+v"(pb_cur[0]), "+v"(pb_cur[1]));
+
+      // ---- one iteration of the fp8-only pipeline, the same code for every s in [-4, nsub):
+      // phase A runs the 32 QK^T MFMAs of sub-tile s+1 with the index load of s+6, the gather of
+      // s+4 and the dequantization of s+2 spread between them; phase B runs the 32 PV MFMAs of
+      // sub-tile s with the softmax of s+1 spread between them. Every step ends in a scheduling
+      // barrier, so each piece stays next to its MFMA. Sub-tiles outside 0..nsub-1 take part with
+      // an all-invalid mask: they gather from a valid dummy address, dequantize to zeros, get zero
+      // probabilities and add nothing.
+      auto fp8_iteration = [&](int s) {
+        const int lane = lane_id();
+        const int t = lane & 31, hh = lane >> 5;
+        // phase A operands
+        uint32_t ka[8];
+        slot_addr(k_addr, (s + 7) % 3, ka);
+        bf16x8 kb[6];
+#pragma unroll
+        for (int i = 0; i < 3; ++i) kb[i] = lds_k(ka[i]);
+        f32x16 s_acc;
+        // dequantization of s+2: this lane's 4 chunks of 16 values
+        const char* draw = raws + ((s + 8) % 3) * kRawBytes;
+        char* trow = tiles + ((s + 8) % 3) * kTileBytes + t * kTileStride;
+        const int sw = tile_swizzle(t);
+        const int c0 = 8 * wave + 4 * hh;
+        const bool dvalid = (mk2 >> t) & 1u;
+        uint32_t sc2 = 0;
+        u32x4 rr[4];
+        bf16x8 dlo, dhi;
+        // gather of s+4
+        const bool g_live = s + 4 < nsub && p.topk > 0;
+        const int g_pos0 = s + 4 < nsub ? locate<EXTRA>(p, t0, s + 4).pos0 : 0;
+        const char* gidx = idx_ring + ((s + 10) % 3) * kIdxBytes;
+        const uint32_t graw = __builtin_amdgcn_readfirstlane(lds_addr(raws + ((s + 10) % 3) * kRawBytes));
+        int gv = 0;
+        const uint8_t* grec = nullptr;
+        const uint8_t* gdat = nullptr;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+          if (i + 3 < 32) kb[(i + 3) % 6] = lds_k(ka[(i + 3) & 7] + 256 * ((i + 3) >> 3));
+          if (i == 0) mfma_qk_first(s_acc, kb[0], qreg[0]);
+          else mfma_qk(s_acc, kb[i % 6], qreg[i]);
+          if (i == 1) {
+            sc2 = *reinterpret_cast<const uint16_t*>(draw + (32 * kSubTokens + t) * 16 + c0 / 2);
+            rr[0] = lds_read16(draw + ((c0 + 0) * kSubTokens + t) * 16);
+            rr[1] = lds_read16(draw + ((c0 + 1) * kSubTokens + t) * 16);
+          } else if (i == 2) {
+            rr[2] = lds_read16(draw + ((c0 + 2) * kSubTokens + t) * 16);
+            rr[3] = lds_read16(draw + ((c0 + 3) * kSubTokens + t) * 16);
+            gv = *reinterpret_cast<const int*>(gidx + 4 * t);
+          } else if (i == 3) {
+            const bool valid = g_live && g_pos0 + t < p.topk && gv >= 0;
+            mk4 = (uint32_t)__ballot(valid);
+            // ignored tokens read record 0; a sub-tile with no records at all reads the query
+            // instead (a valid address of at least 1 KB), so every copy below is always issued
+            grec = g_live ? p.kc + (int64_t)(valid ? gv : 0) * kFp8Rec
+                          : reinterpret_cast<const uint8_t*>(p.q);
+            gdat = grec + 32 * wave + 16 * hh;               // chunk 2(w + 4i) + hh at +128 i
+          } else if (i >= 4 && i < 8) {
+            const int q = wave + 4 * (i - 4);
+            const uint32_t dst = __builtin_amdgcn_readfirstlane(graw + 1024 * q);
+            if (i == 4) copy16_to_lds_off<0>(gdat, dst);
+            else if (i == 5) copy16_to_lds_off<128>(gdat, dst);
+            else if (i == 6) copy16_to_lds_off<256>(gdat, dst);
+            else copy16_to_lds_off<384>(gdat, dst);
+          } else if (i == 8) {
+            copy16_to_lds_masked(grec + 512, __builtin_amdgcn_readfirstlane(graw + 32 * 512), scale_lanes_fp8);
+          } else if (i == 9) {
+            load_indices(s + 6);
+            // ignored tokens of sub-tile s+2 decode as zeros: e4m3 code 0 (+0) with a finite scale
+            // (byte 127 = 1.0; the fetched bytes of an ignored token may hold the e8m0 NaN code)
+            if (mk2 != 0xFFFFFFFFu && !dvalid) {
+#pragma unroll
+              for (int cc = 0; cc < 4; ++cc) rr[cc] = u32x4{};
+              sc2 = 0x7F7Fu;
+            }
+          } else if (i >= 10 && i < 26) {
+            const int cc = (i - 10) >> 2, part = (i - 10) & 3;
+            const uint32_t sb = (sc2 >> (8 * (cc >> 1))) & 0xFFu;
+            if (part == 0) dlo = dequant_fp8_8(rr[cc][0], rr[cc][1], sb);
+            else if (part == 1) dhi = dequant_fp8_8(rr[cc][2], rr[cc][3], sb);
+            else if (part == 2) {
+              lds_write16(trow + 16 * ((2 * (c0 + cc)) ^ sw), __builtin_bit_cast(u32x4, dlo));
+              lds_write16(trow + 16 * ((2 * (c0 + cc) + 1) ^ sw), __builtin_bit_cast(u32x4, dhi));
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        // the scores are read by VALU instructions next: 20 wait states after the last MFMA
+        asm volatile("s_nop 15\n\ts_nop 3" : "+v"(s_acc));
+
+        // phase B: PV of sub-tile s with the softmax of sub-tile s+1
+        uint32_t va[8];
+        slot_addr(v_addr, (s + 6) % 3, va);
+        bf16x8 vb[6];
+#pragma unroll
+        for (int i = 0; i < 3; ++i)
+          vb[i] = lds_v(va[i & 3] + 256 * (i >> 2), va[4 + (i & 3)] + 256 * (i >> 2));
+        bf16x8 pb_new[2];
+        SoftmaxTemps st;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+          if (i + 3 < 32) {
+            const int n = i + 3, nks = n >> 4, nd = n & 15;
+            const uint32_t off = 16384 * nks + 256 * (nd >> 2);
+            vb[n % 6] = lds_v(va[nd & 3] + off, va[4 + (nd & 3)] + off);
+          }
+          mfma_pv(oacc[i & 15], vb[i % 6], pb_cur[i >> 4]);
+          if (i < 16) softmax_step(st, i, s_acc, mk1, pb_new);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        pb_cur[0] = pb_new[0];
+        pb_cur[1] = pb_new[1];
+      };
+
+      load_indices(0);                        // "iteration -6"
+      load_indices(1);                        // "iteration -5"
+
+#pragma clang loop unroll(disable)
+      for (int s = -4; s < nsub; ++s) {
+        // Top of iteration s: idx(s+4) and the gather of sub-tile s+2 (issued in iteration s-2)
+        // have landed once only iteration s-1's operations (idx(s+5), gather(s+3)) may still be
+        // pending.
+        if constexpr (!EXTRA) {
+          // every iteration issues one index load and kGatherFp8 gather copies ("iteration -5"
+          // issued only the index load)
+          wait_and_barrier(s == -4 ? 1 : 1 + kGatherFp8);
+          fp8_iteration(s);
+        } else {
+          wait_and_barrier(1 + gather_count(s + 3));
+          load_indices(s + 6);
+          if (s + 4 >= 0 && s + 4 < nsub) mk4 = gather(s + 4);
+          // QK^T of sub-tile s+1 (tile (s+1) % 3).
+          const bool do_qk = s + 1 >= 0 && s + 1 < nsub && mk1 != 0;
+          f32x16 s_new = f32x16{};
+          if (do_qk) {
+            uint32_t a[8];
+            slot_addr(k_addr, (s + 1) % 3, a);
+            s_new = qk_chain(a, qreg);
+          }
+          // PV of sub-tile s, softmax of sub-tile s+1, dequantization of sub-tile s+2.
+          if (s >= 0 && mk0 != 0) {
+            uint32_t a[8];
+            slot_addr(v_addr, s % 3, a);
+            pv_chain(a, oacc, pb_cur);
+          }
+          if (do_qk) softmax(s_new, mk1, pb_cur);
+          if (s + 2 >= 0 && s + 2 < nsub && mk2 != 0) dequant(s + 2, mk2);
+        }
+
+        mk0 = mk1;
+        mk1 = mk2;
+        mk2 = mk3;
+        mk3 = mk4;
+        mk4 = 0;
+      }
+      // O is read by VALU instructions below: 20 wait states after the last PV MFMA, which writes
+      // block 15 (every other block was written at least one MFMA, 32 cycles, earlier).
+      // The last iterations' copies (dummy gathers and index loads past the segment) are awaited
+      // here, before this workgroup's LDS is reused or released.
+      asm volatile("s_waitcnt vmcnt(0)\n\ts_nop 15\n\ts_nop 3" : "+a"(oacc[15]) :: "memory");
+
+      // A second pass is needed when some head's probabilities relative to m_ref could have
+      // overflowed; the decision has to be the same for the whole workgroup.
+      if (pass > 0) break;
+      const bool any_big = __ballot(m_max > m_ref + kRefSlack) != 0;   // all lanes vote
+      if (lane_id() == 0) redo_flags[wave] = any_big ? 1 : 0;
+      wait_and_barrier(0);
+      const bool redo = (redo_flags[0] | redo_flags[1] | redo_flags[2] | redo_flags[3]) != 0;
+      wait_and_barrier(0);                    // everyone has read the flags
+      if (!redo) break;
+      m_ref_next = m_max;
+    }
+
+    // ---- epilogue of this row segment. O^T block d: lane l holds head l%32 and dims
+    // 32d + 8(r/4) + 4(l/32) + r%4. Blocks are written one at a time.
+    {
+      const int lane = lane_id();
+      const int g = lane >> 5;
+      const int head = head_base + (lane & 31);
+      const bool final_out = nsplit == 1;
+      if (head < p.h_q) {
+        const float inv = l_sum > 0.0f ? 1.0f / l_sum : 0.0f;
+#pragma unroll
+        for (int d = 0; d < 16; ++d) {
+#pragma unroll
+          for (int jb = 0; jb < 4; ++jb) {
+            const int dim = 32 * d + 8 * jb + 4 * g;
+            if (final_out) {
+              bf16x4 o;
+#pragma unroll
+              for (int i = 0; i < 4; ++i) o[i] = (__bf16)(oacc[d][4 * jb + i] * inv);
+              *reinterpret_cast<bf16x4*>(p.out + ((int64_t)row * p.h_q + head) * kHeadDim + dim) = o;
+            } else {
+              f32x4 o;
+#pragma unroll
+              for (int i = 0; i < 4; ++i) o[i] = oacc[d][4 * jb + i] * inv;
+              *reinterpret_cast<f32x4*>(p.part_o + ((int64_t)slot * p.h_q + head) * kHeadDim + dim) = o;
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if (g == 0) {
+          const float lse = l_sum > 0.0f ? (m_ref + __log2f(l_sum)) * 0.69314718055994530942f
+                                         : -__builtin_inff();
+          if (final_out)
+            p.lse[(int64_t)row * p.h_q + head] = lse;
+          else
+            p.part_lse[(int64_t)slot * p.h_q + head] = lse;
+        }
+      }
+    }
+    ++row;
+    t0 = 0;
+    first_seg = false;
+  }
+}
+
+}  // namespace
+
+int launch_sparse_decode_wide(const DecodeParams& p, int parts, int groups, hipStream_t stream) {
+  dim3 grid(parts, groups);
+  if (p.extra_topk > 0)
+    hipLaunchKernelGGL(sparse_decode_wide_kernel<true>, grid, dim3(64 * kWaves), 0, stream, p);
+  else
+    hipLaunchKernelGGL(sparse_decode_wide_kernel<false>, grid, dim3(64 * kWaves), 0, stream, p);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+}  // namespace mla

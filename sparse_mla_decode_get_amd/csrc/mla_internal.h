@@ -25,6 +25,8 @@ struct DecodeParams {
 };
 
 int launch_sparse_decode(const DecodeParams& p, int parts, int groups, int nw, hipStream_t stream);
+// 128-head groups, four waves of 32 heads each (mla_decode_wide.hip).
+int launch_sparse_decode_wide(const DecodeParams& p, int parts, int groups, hipStream_t stream);
 int launch_metadata(int rows, int tiles, int parts, int32_t* sched, int32_t* split_ptr,
                     hipStream_t stream);
 int launch_combine(const float* partial, const float* partial_lse, const int32_t* split_ptr,

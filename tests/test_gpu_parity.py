@@ -128,6 +128,10 @@ SMALL = [
     Spec("mixed_h128", 2, 2, 128, 64, 1024, extra_topk=200, extra_tokens_per_seq=1024,
          values="spread"),
     Spec("fp4_only_extra", 2, 1, 32, 0, 64, extra_topk=100, extra_tokens_per_seq=512),
+    Spec("fp4_only_h128", 2, 1, 128, 0, 64, extra_topk=100, extra_tokens_per_seq=512),
+    Spec("all_ignored_h128", 2, 1, 128, 300, 1024, neg="all"),
+    Spec("h128_ragged_long", 1, 2, 128, 1000, 8192, neg="frac5"),
+    Spec("h128_topk20", 2, 1, 128, 20, 512),
 ]
 
 
@@ -153,6 +157,26 @@ def test_decode_split_rows(spec, parts, min_tiles):
     if spec.name != "one_part":
         assert md.workspace is not None            # some row really is split
     ref_out, ref_lse = _oracle(w)
+    check_rows(out, lse, ref_out, ref_lse, spec.name)
+
+
+def test_scores_growing_past_the_first_subtile():
+    """Later tokens carry 2^8-times larger values, so scores grow by far more than 2^64 over the
+    first 32 tokens' maximum: the decode must still match (a probability reference taken from the
+    first tokens alone would overflow)."""
+    spec = Spec("growth", 1, 1, 128, 300, 2048)
+    w = make_workload(spec, seed=21)
+    later = np.unique(w["indices"][0, 0, 32:])
+    later = later[later >= 0]
+    first = set(w["indices"][0, 0, :32].tolist())
+    later = np.array([t for t in later if t not in first], dtype=np.int64)
+    kc = w["k_cache"].copy()
+    kc[later, 512:] += 8                          # e8m0 scale bytes: values x 256
+    assert kc[later, 512:].max() <= 246
+    w["k_cache"] = kc
+    out, lse, _ = _decode(w)
+    ref_out, ref_lse = _oracle(w)
+    assert (ref_lse.max() - 0) > 40               # the scores really are large
     check_rows(out, lse, ref_out, ref_lse, spec.name)
 
 

@@ -8,6 +8,9 @@ compiler itself inserts for these cases):
   * an MFMA writes registers that a non-MFMA instruction then reads: 12 wait states for the
     8-pass v_mfma_f32_32x32x16_bf16 (a following MFMA reading them as its accumulator input is
     forwarded and needs none).
+It also rejects, conservatively, an MFMA whose result registers overlap its A or B operand (inline
+assembly outputs without an early-clobber constraint can be given such registers; the compiler's
+own MFMAs never are).
 Each instruction counts as one wait state, s_nop N as N + 1. Branches end the window conservatively
 (the scan is linear over the text).
 """
@@ -61,6 +64,8 @@ def check(text, kernel):
             continue
         op, ops = _operands(t)
         if op.startswith("v_mfma"):
+            if _regs(ops[0]) & (_regs(ops[1]) | _regs(ops[2])):
+                problems.append(f"MFMA result overlaps its A/B operand: {t}")
             reads = set()
             for o in ops[1:4]:
                 reads |= _regs(o)

@@ -33,6 +33,21 @@
 namespace mla {
 namespace {
 
+// One all-zero fp8 record (its e8m0 scale byte 0 decodes to the scale 0.0): the gather source of
+// ignored tokens and of sub-tiles outside the segment in the fp8 pipeline, so that their rows
+// dequantize to exact zeros whatever the cache holds. The nonzero tag after the record gives the
+// object an explicit initializer, so its zeros are stored in the code object (read-only data)
+// instead of an uninitialized section.
+struct alignas(16) ZeroRecord {
+  uint8_t bytes[1024];
+  uint32_t tag;
+};
+__device__ const ZeroRecord g_zero = {{}, 1u};
+
+// Score added to ignored tokens by the extra QK^T k-step (bf16 -2^100): after scaling it is far
+// below any real score, so its probability is exactly 0 and it never wins a maximum.
+constexpr uint32_t kIgnoredScoreBits = 0xF180u;
+
 constexpr int kWaves = 4;
 constexpr int kGroupHeads = 32 * kWaves;
 // bf16 tile: token row r at r * 1024 bytes; its 16-byte chunk c (dims 8c .. 8c+7) is stored at
@@ -134,7 +149,7 @@ __device__ __forceinline__ void copy4_to_lds_masked(const void* gptr, uint32_t l
 // One MFMA step as an assembly statement: QK^T (scores in VGPRs, chained) and PV (O in the
 // accumulation registers). Used where other work is interleaved between the steps.
 __device__ __forceinline__ void mfma_qk_first(f32x16& s, const bf16x8& k, const bf16x8& q) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(s) : "v"(k), "v"(q));
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(s) : "v"(k), "v"(q));
 }
 __device__ __forceinline__ void mfma_qk(f32x16& s, const bf16x8& k, const bf16x8& q) {
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(k), "v"(q));
@@ -485,9 +500,12 @@ void sparse_decode_wide_kernel(DecodeParams p) {
   const uint64_t scale_lanes_fp4 = scale_lanes_fp8 | (scale_lanes_fp8 << 32);
 
   if constexpr (!EXTRA) {
-    // The fp8 pipeline's first iterations read tile slots no sub-tile has been written to yet
-    // (with zero probabilities); zeros keep those products finite.
-    for (int o = threadIdx.x * 16; o < kStages * kTileBytes; o += 64 * kWaves * 16)
+    // The fp8 pipeline's first iterations read tile slots no sub-tile has been written to yet,
+    // and dequantize raw slots no gather has filled yet (sub-tiles -2 and -1, with zero
+    // probabilities). Zeros in both keep those scores and products finite: the ignored-token score
+    // masks a finite score, not a NaN. Later segments find finite data of earlier sub-tiles there.
+    static_assert(kOffRaw == kStages * kTileBytes, "raw slots follow the tiles");
+    for (int o = threadIdx.x * 16; o < kOffRaw + kStages * kRawBytes; o += 64 * kWaves * 16)
       lds_write16(tiles + o, u32x4{});
     __syncthreads();
   }
@@ -757,6 +775,53 @@ void sparse_decode_wide_kernel(DecodeParams p) {
           l_sum += sum_xor32(ls);
         }
       };
+      // The same for the fp8 pipeline, whose scores of ignored tokens already hold the ignored
+      // score (no masking), with the scale folded into the exponent: steps 0-3 the maximum of 4 raw
+      // scores each, 4 the reference (live: the sub-tile has a valid token), 5-12 two
+      // exponentials each, 13-14 the P^T operand, 15 the sum.
+      auto softmax_step_fp8 = [&](SoftmaxTemps& st, int step, const f32x16& sv, bool live,
+                                  bf16x8 (&pb)[2]) {
+        float (&e)[16] = st.e;
+        float& mx = st.mx;
+        float& ls = st.ls;
+        if (step < 4) {
+          const float m4 = fmaxf(fmaxf(sv[4 * step], sv[4 * step + 1]), fmaxf(sv[4 * step + 2], sv[4 * step + 3]));
+          if (step == 0) { mx = m4; ls = 0.0f; }
+          else mx = fmaxf(mx, m4);
+        } else if (step == 4) {
+          // the scale is positive: the maximum of the scaled scores is the scaled maximum
+          mx = max_xor32(mx) * p.scale_log2;
+          m_max = live ? fmaxf(m_max, mx) : m_max;
+          m_ref = (live && m_ref == -__builtin_inff()) ? mx : m_ref;
+          // while no valid token has been seen (m_ref = -inf) every score is the ignored score
+          mx = m_ref == -__builtin_inff() ? 0.0f : -m_ref;   // reused as the exponent offset
+        } else if (step < 13) {
+#pragma unroll
+          for (int r = 2 * (step - 5); r < 2 * (step - 5) + 2; ++r) {
+            e[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[r], p.scale_log2, mx));
+            ls += e[r];
+          }
+        } else if (step < 15) {
+          const int ks = step - 13;
+          uint32_t xw[2], yw[2];
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            bf16x2 xa, ya;
+            xa[0] = (__bf16)e[8 * ks + 2 * h];
+            xa[1] = (__bf16)e[8 * ks + 2 * h + 1];
+            ya[0] = (__bf16)e[8 * ks + 4 + 2 * h];
+            ya[1] = (__bf16)e[8 * ks + 4 + 2 * h + 1];
+            auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, xa),
+                                                       __builtin_bit_cast(uint32_t, ya), false, false);
+            xw[h] = (uint32_t)sw[0];
+            yw[h] = (uint32_t)sw[1];
+          }
+          const u32x4 packed = {xw[0], xw[1], yw[0], yw[1]};
+          pb[ks] = __builtin_bit_cast(bf16x8, packed);
+        } else if (step == 15) {
+          l_sum += sum_xor32(ls);
+        }
+      };
       auto softmax = [&](const f32x16& sv, uint32_t mask, bf16x8 (&pb)[2]) {
         SoftmaxTemps st;
 #pragma unroll
@@ -766,6 +831,9 @@ void sparse_decode_wide_kernel(DecodeParams p) {
       // Validity masks of sub-tiles s .. s+4 (scalar ring) and the P^T operand of sub-tile s.
       uint32_t mk0 = 0, mk1 = 0, mk2 = 0, mk3 = 0, mk4 = 0;
       bf16x8 pb_cur[2] = {bf16x8{}, bf16x8{}};
+      // K operand ring of the fp8 pipeline; between iterations kb[0..2] hold the first three
+      // operands of the next QK^T
+      bf16x8 kb[5];
       // opaque, so that no copy of the loop is specialised for this constant
       asm volatile("" : "+v"(pb_cur[0]), "+v"(pb_cur[1]));
 
@@ -779,19 +847,31 @@ void sparse_decode_wide_kernel(DecodeParams p) {
       auto fp8_iteration = [&](int s) {
         const int lane = lane_id();
         const int t = lane & 31, hh = lane >> 5;
-        // phase A operands
-        uint32_t ka[8];
+        // operand addresses: K of sub-tile s+1 (phase A), V of sub-tile s (phase B); kb[0..2]
+        // already hold the first three K operands
+        uint32_t ka[8], va[8];
         slot_addr(k_addr, (s + 7) % 3, ka);
-        bf16x8 kb[6];
-#pragma unroll
-        for (int i = 0; i < 3; ++i) kb[i] = lds_k(ka[i]);
+        slot_addr(v_addr, (s + 6) % 3, va);
+        bf16x8 vb[5];
         f32x16 s_acc;
+        // A operand of the extra k-step: lane l (token l%32, dims 8(l/32) ..) holds bf16 1.0 in
+        // dim 1 if token l%32 of sub-tile s+1 is ignored (lanes 0..31 only)
+        // and the B operand: lane l (head l%32, dims 8(l/32) ..) holds the ignored score in dim 1
+        // (lanes 0..31). Both are rebuilt every iteration instead of occupying registers.
+        bf16x8 kflag, qflag;
+        {
+          uint32_t f0, g0 = kIgnoredScoreBits << 16;
+          const uint64_t ign = (uint64_t)(uint32_t)~mk1;
+          asm volatile("v_cndmask_b32_e64 %0, 0, 1.0, %1" : "=v"(f0) : "s"(ign));
+          asm volatile("v_cndmask_b32_e64 %0, 0, %0, %1" : "+v"(g0) : "s"(0xFFFFFFFFull));
+          kflag = __builtin_bit_cast(bf16x8, u32x4{f0, 0u, 0u, 0u});
+          qflag = __builtin_bit_cast(bf16x8, u32x4{g0, 0u, 0u, 0u});
+        }
         // dequantization of s+2: this lane's 4 chunks of 16 values
         const char* draw = raws + ((s + 8) % 3) * kRawBytes;
         char* trow = tiles + ((s + 8) % 3) * kTileBytes + t * kTileStride;
         const int sw = tile_swizzle(t);
         const int c0 = 8 * wave + 4 * hh;
-        const bool dvalid = (mk2 >> t) & 1u;
         uint32_t sc2 = 0;
         u32x4 rr[4];
         bf16x8 dlo, dhi;
@@ -805,9 +885,16 @@ void sparse_decode_wide_kernel(DecodeParams p) {
         const uint8_t* gdat = nullptr;
 #pragma unroll
         for (int i = 0; i < 32; ++i) {
-          if (i + 3 < 32) kb[(i + 3) % 6] = lds_k(ka[(i + 3) & 7] + 256 * ((i + 3) >> 3));
-          if (i == 0) mfma_qk_first(s_acc, kb[0], qreg[0]);
-          else mfma_qk(s_acc, kb[i % 6], qreg[i]);
+          // operands are read three MFMAs ahead, into phase B's first V operands at the end
+          if (i + 3 < 32) kb[(i + 3) % 5] = lds_k(ka[(i + 3) & 7] + 256 * ((i + 3) >> 3));
+          else vb[i - 29] = lds_v(va[i - 29], va[4 + i - 29]);
+          if (i == 0) {
+            // extra k-step: the ignored score for ignored tokens of s+1, +0 for the others
+            mfma_qk_first(s_acc, kflag, qflag);
+            mfma_qk(s_acc, kb[0], qreg[0]);
+          } else {
+            mfma_qk(s_acc, kb[i % 5], qreg[i]);
+          }
           if (i == 1) {
             sc2 = *reinterpret_cast<const uint16_t*>(draw + (32 * kSubTokens + t) * 16 + c0 / 2);
             rr[0] = lds_read16(draw + ((c0 + 0) * kSubTokens + t) * 16);
@@ -819,10 +906,9 @@ void sparse_decode_wide_kernel(DecodeParams p) {
           } else if (i == 3) {
             const bool valid = g_live && g_pos0 + t < p.topk && gv >= 0;
             mk4 = (uint32_t)__ballot(valid);
-            // ignored tokens read record 0; a sub-tile with no records at all reads the query
-            // instead (a valid address of at least 1 KB), so every copy below is always issued
-            grec = g_live ? p.kc + (int64_t)(valid ? gv : 0) * kFp8Rec
-                          : reinterpret_cast<const uint8_t*>(p.q);
+            // ignored tokens and sub-tiles outside the segment read the zero record, so every copy
+            // below is always issued
+            grec = valid ? p.kc + (int64_t)gv * kFp8Rec : g_zero.bytes;
             gdat = grec + 32 * wave + 16 * hh;               // chunk 2(w + 4i) + hh at +128 i
           } else if (i >= 4 && i < 8) {
             const int q = wave + 4 * (i - 4);
@@ -835,13 +921,6 @@ void sparse_decode_wide_kernel(DecodeParams p) {
             copy16_to_lds_masked(grec + 512, __builtin_amdgcn_readfirstlane(graw + 32 * 512), scale_lanes_fp8);
           } else if (i == 9) {
             load_indices(s + 6);
-            // ignored tokens of sub-tile s+2 decode as zeros: e4m3 code 0 (+0) with a finite scale
-            // (byte 127 = 1.0; the fetched bytes of an ignored token may hold the e8m0 NaN code)
-            if (mk2 != 0xFFFFFFFFu && !dvalid) {
-#pragma unroll
-              for (int cc = 0; cc < 4; ++cc) rr[cc] = u32x4{};
-              sc2 = 0x7F7Fu;
-            }
           } else if (i >= 10 && i < 26) {
             const int cc = (i - 10) >> 2, part = (i - 10) & 3;
             const uint32_t sb = (sc2 >> (8 * (cc >> 1))) & 0xFFu;
@@ -854,16 +933,8 @@ void sparse_decode_wide_kernel(DecodeParams p) {
           }
           __builtin_amdgcn_sched_barrier(0);
         }
-        // the scores are read by VALU instructions next: 20 wait states after the last MFMA
-        asm volatile("s_nop 15\n\ts_nop 3" : "+v"(s_acc));
 
         // phase B: PV of sub-tile s with the softmax of sub-tile s+1
-        uint32_t va[8];
-        slot_addr(v_addr, (s + 6) % 3, va);
-        bf16x8 vb[6];
-#pragma unroll
-        for (int i = 0; i < 3; ++i)
-          vb[i] = lds_v(va[i & 3] + 256 * (i >> 2), va[4 + (i & 3)] + 256 * (i >> 2));
         bf16x8 pb_new[2];
         SoftmaxTemps st;
 #pragma unroll
@@ -871,10 +942,21 @@ void sparse_decode_wide_kernel(DecodeParams p) {
           if (i + 3 < 32) {
             const int n = i + 3, nks = n >> 4, nd = n & 15;
             const uint32_t off = 16384 * nks + 256 * (nd >> 2);
-            vb[n % 6] = lds_v(va[nd & 3] + off, va[4 + (nd & 3)] + off);
+            vb[n % 5] = lds_v(va[nd & 3] + off, va[4 + (nd & 3)] + off);
           }
-          mfma_pv(oacc[i & 15], vb[i % 6], pb_cur[i >> 4]);
-          if (i < 16) softmax_step(st, i, s_acc, mk1, pb_new);
+          mfma_pv(oacc[i & 15], vb[i % 5], pb_cur[i >> 4]);
+          // the scores are read by VALU instructions next: 20 wait states after the last QK^T
+          // MFMA (the PV MFMA above runs meanwhile)
+          if (i == 0) asm volatile("s_nop 15\n\ts_nop 3" : "+v"(s_acc));
+          if (i < 16) softmax_step_fp8(st, i, s_acc, mk1 != 0, pb_new);
+          if (i == 29) {
+            // Start of iteration s+1, while PV MFMAs 29..31 (operands in registers) still run:
+            // every V read of this iteration is complete, idx(s+5) and the gather of s+3 (issued
+            // in iteration s-1) have landed and all waves' dequantization of s+2 is written, so
+            // the first K operands of QK^T(s+2) can be read.
+            wait_and_barrier(1 + kGatherFp8);
+          }
+          if (i >= 29) kb[i - 29] = lds_k(k_addr[i - 29] + ((s + 8) % 3) * kTileBytes);
           __builtin_amdgcn_sched_barrier(0);
         }
         pb_cur[0] = pb_new[0];
@@ -883,6 +965,12 @@ void sparse_decode_wide_kernel(DecodeParams p) {
 
       load_indices(0);                        // "iteration -6"
       load_indices(1);                        // "iteration -5"
+      if constexpr (!EXTRA) {
+        // start of iteration -4: idx(0) has landed ("iteration -5" issued only idx(1))
+        wait_and_barrier(1);
+#pragma unroll
+        for (int n = 0; n < 3; ++n) kb[n] = lds_k(k_addr[n] + ((-4 + 7) % 3) * kTileBytes);
+      }
 
 #pragma clang loop unroll(disable)
       for (int s = -4; s < nsub; ++s) {
@@ -890,9 +978,8 @@ void sparse_decode_wide_kernel(DecodeParams p) {
         // have landed once only iteration s-1's operations (idx(s+5), gather(s+3)) may still be
         // pending.
         if constexpr (!EXTRA) {
-          // every iteration issues one index load and kGatherFp8 gather copies ("iteration -5"
-          // issued only the index load)
-          wait_and_barrier(s == -4 ? 1 : 1 + kGatherFp8);
+          // the iteration's wait and barrier are issued by the previous iteration (every
+          // iteration issues one index load and kGatherFp8 gather copies) or before the loop
           fp8_iteration(s);
         } else {
           wait_and_barrier(1 + gather_count(s + 3));

@@ -10,7 +10,7 @@ compiler itself inserts for these cases):
     forwarded and needs none).
 It also rejects, conservatively, an MFMA whose result registers overlap its A or B operand (inline
 assembly outputs without an early-clobber constraint can be given such registers; the compiler's
-own MFMAs never are).
+own MFMAs never are). m0_outside_inline_asm() lists compiler-generated instructions that use m0.
 Each instruction counts as one wait state, s_nop N as N + 1. Branches end the window conservatively
 (the scan is linear over the text).
 """
@@ -93,6 +93,28 @@ def check(text, kernel):
                     problems.append(f"MFMA result used {ws} wait states later: {t} -> {u}")
                 ws += int(uops[0]) + 1 if uop == "s_nop" else 1
     return problems
+
+
+def m0_outside_inline_asm(text, kernel):
+    """Instructions of `kernel` outside inline-assembly blocks that name m0. The kernels' LDS copies
+    set m0 inside their own assembly and leave it set, which is only sound while no
+    compiler-generated instruction relies on m0."""
+    lines = text.split("\n")
+    start = next(i for i, l in enumerate(lines) if l.split(";")[0].strip() == kernel + ":")
+    out, in_asm = [], False
+    for l in lines[start + 1:]:
+        if ";;#ASMSTART" in l:
+            in_asm = True
+            continue
+        if ";;#ASMEND" in l:
+            in_asm = False
+            continue
+        t = l.split(";")[0].strip()
+        if not in_asm and re.search(r"\bm0\b", t):
+            out.append(f"m0 used outside inline assembly: {t}")
+        if t.startswith("s_endpgm"):
+            break
+    return out
 
 
 def kernels(text, name_part):

@@ -7,8 +7,9 @@ while scratch stays at zero: on gfx950 they go to spare VGPR lanes (v_writelane 
 never reach memory. The per-kernel report is written to _build/kernel_resources.txt.
 
 Sources whose kernels contain MFMAs written as inline assembly are also compiled to device
-assembly and checked for the wait states gfx950 requires around those MFMAs (asm_check.py); the
-build fails on any violation.
+assembly and checked for the wait states gfx950 requires around those MFMAs, and for
+compiler-generated uses of m0, which the kernels' LDS copies leave set (asm_check.py); the build
+fails on any violation.
 
 Usage: python -m sparse_mla_decode_get_amd.build   (or build() from Python)
 """
@@ -62,6 +63,7 @@ def _asm_check(src, name_part):
     problems = []
     for k in names:
         problems += [f"{k}: {m}" for m in asm_check.check(text, k)]
+        problems += [f"{k}: {m}" for m in asm_check.m0_outside_inline_asm(text, k)]
     return problems
 
 

@@ -83,18 +83,16 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 }
 
 // 16-byte and 4-byte global -> LDS copies: the wave's active lanes write LDS bytes m0 + 16 * lane
-// (resp. m0 + 4 * lane). m0 is saved and restored; `lds_base` must be wave-uniform. The masked
+// (resp. m0 + 4 * lane). m0 is set and not restored: no compiler-generated code of these kernels
+// reads m0 (the build's assembly check rejects any that does). `lds_base` must be wave-uniform. The masked
 // forms run the copy with EXEC = `lanes` (wave-uniform, never 0) and restore EXEC afterwards, so
 // that a partial-wave copy needs no branch around it.
 __device__ __forceinline__ void copy16_to_lds(const void* gptr, uint32_t lds_base) {
-  uint32_t saved;
   asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
+      "s_mov_b32 m0, %0\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %2, off\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
+      "global_load_lds_dwordx4 %1, off"
+      :
       : "s"(lds_base), "v"(gptr)
       : "memory");
 }
@@ -102,46 +100,37 @@ __device__ __forceinline__ void copy16_to_lds(const void* gptr, uint32_t lds_bas
 // (LDS address = m0 + offset + 16 * lane), so m0 is set to lds_base - OFF.
 template <int OFF>
 __device__ __forceinline__ void copy16_to_lds_off(const void* gptr, uint32_t lds_base) {
-  uint32_t saved;
   asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
+      "s_mov_b32 m0, %0\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %2, off offset:%3\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
+      "global_load_lds_dwordx4 %1, off offset:%2"
+      :
       : "s"(lds_base - OFF), "v"(gptr), "i"(OFF)
       : "memory");
 }
 __device__ __forceinline__ void copy16_to_lds_masked(const void* gptr, uint32_t lds_base, uint64_t lanes) {
-  uint32_t saved;
   uint64_t saved_exec;
   asm volatile(
-      "s_mov_b64 %1, exec\n\t"
-      "s_mov_b64 exec, %4\n\t"
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %2\n\t"
+      "s_mov_b64 %0, exec\n\t"
+      "s_mov_b64 exec, %3\n\t"
+      "s_mov_b32 m0, %1\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %3, off\n\t"
-      "s_mov_b32 m0, %0\n\t"
-      "s_mov_b64 exec, %1"
-      : "=&s"(saved), "=&s"(saved_exec)
+      "global_load_lds_dwordx4 %2, off\n\t"
+      "s_mov_b64 exec, %0"
+      : "=&s"(saved_exec)
       : "s"(lds_base), "v"(gptr), "s"(lanes)
       : "memory");
 }
 __device__ __forceinline__ void copy4_to_lds_masked(const void* gptr, uint32_t lds_base, uint64_t lanes) {
-  uint32_t saved;
   uint64_t saved_exec;
   asm volatile(
-      "s_mov_b64 %1, exec\n\t"
-      "s_mov_b64 exec, %4\n\t"
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %2\n\t"
+      "s_mov_b64 %0, exec\n\t"
+      "s_mov_b64 exec, %3\n\t"
+      "s_mov_b32 m0, %1\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dword %3, off\n\t"
-      "s_mov_b32 m0, %0\n\t"
-      "s_mov_b64 exec, %1"
-      : "=&s"(saved), "=&s"(saved_exec)
+      "global_load_lds_dword %2, off\n\t"
+      "s_mov_b64 exec, %0"
+      : "=&s"(saved_exec)
       : "s"(lds_base), "v"(gptr), "s"(lanes)
       : "memory");
 }
@@ -546,7 +535,7 @@ void sparse_decode_wide_kernel(DecodeParams p) {
     // entries past the end of the index row are fetched from a clamped address and replaced by
     // -1 when read). It is issued for every iteration: past the last sub-tile, or for a selection
     // of size 0 (no index array), it reads from the schedule instead (a valid address).
-    auto load_indices = [&](int j) {
+    auto load_indices = [&](int j, int slot) {
       const int lane = lane_id();
       const int32_t* src_ptr = p.sched;
       if (j < nsub) {
@@ -554,7 +543,7 @@ void sparse_decode_wide_kernel(DecodeParams p) {
         if (st.count > 0)
           src_ptr = (st.fp4 ? p.xidx : p.idx) + (int64_t)row * st.count + min(st.pos0 + lane, st.count - 1);
       }
-      copy4_to_lds_masked(src_ptr, __builtin_amdgcn_readfirstlane(lds_addr(idx_ring + (j % 3) * kIdxBytes)),
+      copy4_to_lds_masked(src_ptr, __builtin_amdgcn_readfirstlane(lds_addr(idx_ring + slot * kIdxBytes)),
                           0xFFFFFFFFull);
     };
     // Gather of sub-tile j into raw slot j % 3; returns the validity mask of its 32 tokens.
@@ -785,9 +774,14 @@ void sparse_decode_wide_kernel(DecodeParams p) {
         float& mx = st.mx;
         float& ls = st.ls;
         if (step < 4) {
-          const float m4 = fmaxf(fmaxf(sv[4 * step], sv[4 * step + 1]), fmaxf(sv[4 * step + 2], sv[4 * step + 3]));
-          if (step == 0) { mx = m4; ls = 0.0f; }
-          else mx = fmaxf(mx, m4);
+          const int r = 4 * step;
+          if (step == 0) {
+            mx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), sv[2]), sv[3]);
+            ls = 0.0f;
+          } else {
+            mx = fmaxf(fmaxf(mx, sv[r]), sv[r + 1]);
+            mx = fmaxf(fmaxf(mx, sv[r + 2]), sv[r + 3]);
+          }
         } else if (step == 4) {
           // the scale is positive: the maximum of the scaled scores is the scaled maximum
           mx = max_xor32(mx) * p.scale_log2;
@@ -844,32 +838,33 @@ void sparse_decode_wide_kernel(DecodeParams p) {
       // barrier, so each piece stays next to its MFMA. Sub-tiles outside 0..nsub-1 take part with
       // an all-invalid mask: they gather from a valid dummy address, dequantize to zeros, get zero
       // probabilities and add nothing.
-      auto fp8_iteration = [&](int s) {
+      auto fp8_iteration = [&](int s, int r0, int r1, int r2) {
         const int lane = lane_id();
         const int t = lane & 31, hh = lane >> 5;
         // operand addresses: K of sub-tile s+1 (phase A), V of sub-tile s (phase B); kb[0..2]
         // already hold the first three K operands
         uint32_t ka[8], va[8];
-        slot_addr(k_addr, (s + 7) % 3, ka);
-        slot_addr(v_addr, (s + 6) % 3, va);
+        slot_addr(k_addr, r1, ka);
+        slot_addr(v_addr, r0, va);
         bf16x8 vb[5];
         f32x16 s_acc;
         // A operand of the extra k-step: lane l (token l%32, dims 8(l/32) ..) holds bf16 1.0 in
         // dim 1 if token l%32 of sub-tile s+1 is ignored (lanes 0..31 only)
-        // and the B operand: lane l (head l%32, dims 8(l/32) ..) holds the ignored score in dim 1
-        // (lanes 0..31). Both are rebuilt every iteration instead of occupying registers.
+        // and the B operand: lane l (head l%32, dims 8(l/32) ..) holds the ignored score in dim 1.
+        // Both are rebuilt every iteration instead of occupying registers.
         bf16x8 kflag, qflag;
         {
-          uint32_t f0, g0 = kIgnoredScoreBits << 16;
+          // (the B operand's dim 9 in lanes 32..63 also holds the ignored score; A is 0 there)
+          uint32_t f0, g0;
           const uint64_t ign = (uint64_t)(uint32_t)~mk1;
           asm volatile("v_cndmask_b32_e64 %0, 0, 1.0, %1" : "=v"(f0) : "s"(ign));
-          asm volatile("v_cndmask_b32_e64 %0, 0, %0, %1" : "+v"(g0) : "s"(0xFFFFFFFFull));
+          asm volatile("v_mov_b32 %0, %1" : "=v"(g0) : "i"(kIgnoredScoreBits << 16));
           kflag = __builtin_bit_cast(bf16x8, u32x4{f0, 0u, 0u, 0u});
           qflag = __builtin_bit_cast(bf16x8, u32x4{g0, 0u, 0u, 0u});
         }
         // dequantization of s+2: this lane's 4 chunks of 16 values
-        const char* draw = raws + ((s + 8) % 3) * kRawBytes;
-        char* trow = tiles + ((s + 8) % 3) * kTileBytes + t * kTileStride;
+        const char* draw = raws + r2 * kRawBytes;
+        char* trow = tiles + r2 * kTileBytes + t * kTileStride;
         const int sw = tile_swizzle(t);
         const int c0 = 8 * wave + 4 * hh;
         uint32_t sc2 = 0;
@@ -878,8 +873,8 @@ void sparse_decode_wide_kernel(DecodeParams p) {
         // gather of s+4
         const bool g_live = s + 4 < nsub && p.topk > 0;
         const int g_pos0 = s + 4 < nsub ? locate<EXTRA>(p, t0, s + 4).pos0 : 0;
-        const char* gidx = idx_ring + ((s + 10) % 3) * kIdxBytes;
-        const uint32_t graw = __builtin_amdgcn_readfirstlane(lds_addr(raws + ((s + 10) % 3) * kRawBytes));
+        const char* gidx = idx_ring + r1 * kIdxBytes;
+        const uint32_t graw = __builtin_amdgcn_readfirstlane(lds_addr(raws + r1 * kRawBytes));
         int gv = 0;
         const uint8_t* grec = nullptr;
         const uint8_t* gdat = nullptr;
@@ -899,10 +894,10 @@ void sparse_decode_wide_kernel(DecodeParams p) {
             sc2 = *reinterpret_cast<const uint16_t*>(draw + (32 * kSubTokens + t) * 16 + c0 / 2);
             rr[0] = lds_read16(draw + ((c0 + 0) * kSubTokens + t) * 16);
             rr[1] = lds_read16(draw + ((c0 + 1) * kSubTokens + t) * 16);
+            gv = *reinterpret_cast<const int*>(gidx + 4 * t);
           } else if (i == 2) {
             rr[2] = lds_read16(draw + ((c0 + 2) * kSubTokens + t) * 16);
             rr[3] = lds_read16(draw + ((c0 + 3) * kSubTokens + t) * 16);
-            gv = *reinterpret_cast<const int*>(gidx + 4 * t);
           } else if (i == 3) {
             const bool valid = g_live && g_pos0 + t < p.topk && gv >= 0;
             mk4 = (uint32_t)__ballot(valid);
@@ -910,19 +905,22 @@ void sparse_decode_wide_kernel(DecodeParams p) {
             // below is always issued
             grec = valid ? p.kc + (int64_t)gv * kFp8Rec : g_zero.bytes;
             gdat = grec + 32 * wave + 16 * hh;               // chunk 2(w + 4i) + hh at +128 i
-          } else if (i >= 4 && i < 8) {
-            const int q = wave + 4 * (i - 4);
-            const uint32_t dst = __builtin_amdgcn_readfirstlane(graw + 1024 * q);
-            if (i == 4) copy16_to_lds_off<0>(gdat, dst);
-            else if (i == 5) copy16_to_lds_off<128>(gdat, dst);
-            else if (i == 6) copy16_to_lds_off<256>(gdat, dst);
+          }
+          // gather copies at steps 4..8: 4 chunk pairs (wave w moves chunks 2(w + 4c) + hh of all 32
+          // tokens) and the scale chunks of tokens 8w .. 8w+7
+          if (i >= 4 && i < 8) {
+            const int c = i - 4;
+            const uint32_t dst = __builtin_amdgcn_readfirstlane(graw + 1024 * (wave + 4 * c));
+            if (c == 0) copy16_to_lds_off<0>(gdat, dst);
+            else if (c == 1) copy16_to_lds_off<128>(gdat, dst);
+            else if (c == 2) copy16_to_lds_off<256>(gdat, dst);
             else copy16_to_lds_off<384>(gdat, dst);
           } else if (i == 8) {
             copy16_to_lds_masked(grec + 512, __builtin_amdgcn_readfirstlane(graw + 32 * 512), scale_lanes_fp8);
-          } else if (i == 9) {
-            load_indices(s + 6);
-          } else if (i >= 10 && i < 26) {
-            const int cc = (i - 10) >> 2, part = (i - 10) & 3;
+          }
+          if (i == 9) load_indices(s + 6, r0);
+          if (i >= 8 && i < 24) {
+            const int cc = (i - 8) >> 2, part = (i - 8) & 3;
             const uint32_t sb = (sc2 >> (8 * (cc >> 1))) & 0xFFu;
             if (part == 0) dlo = dequant_fp8_8(rr[cc][0], rr[cc][1], sb);
             else if (part == 1) dhi = dequant_fp8_8(rr[cc][2], rr[cc][3], sb);
@@ -956,15 +954,15 @@ void sparse_decode_wide_kernel(DecodeParams p) {
             // the first K operands of QK^T(s+2) can be read.
             wait_and_barrier(1 + kGatherFp8);
           }
-          if (i >= 29) kb[i - 29] = lds_k(k_addr[i - 29] + ((s + 8) % 3) * kTileBytes);
+          if (i >= 29) kb[i - 29] = lds_k(k_addr[i - 29] + r2 * kTileBytes);
           __builtin_amdgcn_sched_barrier(0);
         }
         pb_cur[0] = pb_new[0];
         pb_cur[1] = pb_new[1];
       };
 
-      load_indices(0);                        // "iteration -6"
-      load_indices(1);                        // "iteration -5"
+      load_indices(0, 0);                        // "iteration -6"
+      load_indices(1, 1);                        // "iteration -5"
       if constexpr (!EXTRA) {
         // start of iteration -4: idx(0) has landed ("iteration -5" issued only idx(1))
         wait_and_barrier(1);
@@ -972,6 +970,8 @@ void sparse_decode_wide_kernel(DecodeParams p) {
         for (int n = 0; n < 3; ++n) kb[n] = lds_k(k_addr[n] + ((-4 + 7) % 3) * kTileBytes);
       }
 
+      // slots of sub-tiles s, s+1, s+2 (s % 3 ... for s >= -4), rotated every iteration
+      int r0 = 2, r1 = 0, r2 = 1;
 #pragma clang loop unroll(disable)
       for (int s = -4; s < nsub; ++s) {
         // Top of iteration s: idx(s+4) and the gather of sub-tile s+2 (issued in iteration s-2)
@@ -980,10 +980,10 @@ void sparse_decode_wide_kernel(DecodeParams p) {
         if constexpr (!EXTRA) {
           // the iteration's wait and barrier are issued by the previous iteration (every
           // iteration issues one index load and kGatherFp8 gather copies) or before the loop
-          fp8_iteration(s);
+          fp8_iteration(s, r0, r1, r2);
         } else {
           wait_and_barrier(1 + gather_count(s + 3));
-          load_indices(s + 6);
+          load_indices(s + 6, (s + 6) % 3);
           if (s + 4 >= 0 && s + 4 < nsub) mk4 = gather(s + 4);
           // QK^T of sub-tile s+1 (tile (s+1) % 3).
           const bool do_qk = s + 1 >= 0 && s + 1 < nsub && mk1 != 0;
@@ -1008,6 +1008,10 @@ void sparse_decode_wide_kernel(DecodeParams p) {
         mk2 = mk3;
         mk3 = mk4;
         mk4 = 0;
+        const int r_old = r0;
+        r0 = r1;
+        r1 = r2;
+        r2 = r_old;
       }
       // O is read by VALU instructions below: 20 wait states after the last PV MFMA, which writes
       // block 15 (every other block was written at least one MFMA, 32 cycles, earlier).

@@ -43,3 +43,11 @@ def test_result_overlapping_an_a_or_b_operand_is_rejected():
     assert any("overlaps" in p for p in _problems([f"{MFMA} v[0:15], v[16:19], v[0:3], 0"]))
     assert any("overlaps" in p for p in _problems([f"{MFMA} v[0:15], v[12:15], v[20:23], 0"]))
     assert _problems([f"{MFMA} v[0:15], v[16:19], v[20:23], 0"]) == []
+
+
+def test_m0_outside_inline_asm_is_reported():
+    text = ("_Zk:\n\t;;#ASMSTART\n\ts_mov_b32 m0, s4\n\tglobal_load_lds_dwordx4 v[0:1], off\n\t;;#ASMEND\n"
+            "\ts_mov_b32 m0, -1\n\tds_write_b32 v0, v1\n\ts_endpgm\n")
+    probs = asm_check.m0_outside_inline_asm(text, "_Zk")
+    assert len(probs) == 1 and "s_mov_b32 m0, -1" in probs[0]
+    assert asm_check.m0_outside_inline_asm(text.replace("\ts_mov_b32 m0, -1\n", ""), "_Zk") == []

@@ -853,15 +853,6 @@ void sparse_decode_wide_kernel(DecodeParams p) {
         // and the B operand: lane l (head l%32, dims 8(l/32) ..) holds the ignored score in dim 1.
         // Both are rebuilt every iteration instead of occupying registers.
         bf16x8 kflag, qflag;
-        {
-          // (the B operand's dim 9 in lanes 32..63 also holds the ignored score; A is 0 there)
-          uint32_t f0, g0;
-          const uint64_t ign = (uint64_t)(uint32_t)~mk1;
-          asm volatile("v_cndmask_b32_e64 %0, 0, 1.0, %1" : "=v"(f0) : "s"(ign));
-          asm volatile("v_mov_b32 %0, %1" : "=v"(g0) : "i"(kIgnoredScoreBits << 16));
-          kflag = __builtin_bit_cast(bf16x8, u32x4{f0, 0u, 0u, 0u});
-          qflag = __builtin_bit_cast(bf16x8, u32x4{g0, 0u, 0u, 0u});
-        }
         // dequantization of s+2: this lane's 4 chunks of 16 values
         const char* draw = raws + r2 * kRawBytes;
         char* trow = tiles + r2 * kTileBytes + t * kTileStride;
@@ -872,7 +863,7 @@ void sparse_decode_wide_kernel(DecodeParams p) {
         bf16x8 dlo, dhi;
         // gather of s+4
         const bool g_live = s + 4 < nsub && p.topk > 0;
-        const int g_pos0 = s + 4 < nsub ? locate<EXTRA>(p, t0, s + 4).pos0 : 0;
+        const int g_pos0 = kUnitTokens * t0 + kSubTokens * (s + 4);   // fp8 sub-tile s+4
         const char* gidx = idx_ring + r1 * kIdxBytes;
         const uint32_t graw = __builtin_amdgcn_readfirstlane(lds_addr(raws + r1 * kRawBytes));
         int gv = 0;
@@ -883,13 +874,11 @@ void sparse_decode_wide_kernel(DecodeParams p) {
           // operands are read three MFMAs ahead, into phase B's first V operands at the end
           if (i + 3 < 32) kb[(i + 3) % 5] = lds_k(ka[(i + 3) & 7] + 256 * ((i + 3) >> 3));
           else vb[i - 29] = lds_v(va[i - 29], va[4 + i - 29]);
-          if (i == 0) {
-            // extra k-step: the ignored score for ignored tokens of s+1, +0 for the others
-            mfma_qk_first(s_acc, kflag, qflag);
-            mfma_qk(s_acc, kb[0], qreg[0]);
-          } else {
-            mfma_qk(s_acc, kb[i % 5], qreg[i]);
-          }
+          if (i == 0) mfma_qk_first(s_acc, kb[0], qreg[0]);
+          else mfma_qk(s_acc, kb[i % 5], qreg[i]);
+          // extra k-step after the last one: the ignored score for ignored tokens of s+1, +0 for
+          // the others (its operands are built two steps earlier)
+          if (i == 31) mfma_qk(s_acc, kflag, qflag);
           if (i == 1) {
             sc2 = *reinterpret_cast<const uint16_t*>(draw + (32 * kSubTokens + t) * 16 + c0 / 2);
             rr[0] = lds_read16(draw + ((c0 + 0) * kSubTokens + t) * 16);
@@ -918,7 +907,25 @@ void sparse_decode_wide_kernel(DecodeParams p) {
           } else if (i == 8) {
             copy16_to_lds_masked(grec + 512, __builtin_amdgcn_readfirstlane(graw + 32 * 512), scale_lanes_fp8);
           }
-          if (i == 9) load_indices(s + 6, r0);
+          if (i == 29) {
+            // (the B operand's dim 9 in lanes 32..63 also holds the ignored score; A is 0 there)
+            uint32_t f0, g0;
+            const uint64_t ign = (uint64_t)(uint32_t)~mk1;
+            asm volatile("v_cndmask_b32_e64 %0, 0, 1.0, %1" : "=v"(f0) : "s"(ign));
+            asm volatile("v_mov_b32 %0, %1" : "=v"(g0) : "i"(kIgnoredScoreBits << 16));
+            kflag = __builtin_bit_cast(bf16x8, u32x4{f0, 0u, 0u, 0u});
+            qflag = __builtin_bit_cast(bf16x8, u32x4{g0, 0u, 0u, 0u});
+          }
+          if (i == 26) {
+            // index load of sub-tile s+6 (fp8: positions 64 t0 + 32 (s+6) ..; past the segment or
+            // for an empty selection it reads the schedule instead, a valid address)
+            const int j = s + 6;
+            const int32_t* src = p.sched;
+            if (j < nsub && p.topk > 0)
+              src = p.idx + (int64_t)row * p.topk + min(kUnitTokens * t0 + kSubTokens * j + lane_id(), p.topk - 1);
+            copy4_to_lds_masked(src, __builtin_amdgcn_readfirstlane(lds_addr(idx_ring + r0 * kIdxBytes)),
+                                0xFFFFFFFFull);
+          }
           if (i >= 8 && i < 24) {
             const int cc = (i - 8) >> 2, part = (i - 8) & 3;
             const uint32_t sb = (sc2 >> (8 * (cc >> 1))) & 0xFFu;
@@ -946,7 +953,7 @@ void sparse_decode_wide_kernel(DecodeParams p) {
           // the scores are read by VALU instructions next: 20 wait states after the last QK^T
           // MFMA (the PV MFMA above runs meanwhile)
           if (i == 0) asm volatile("s_nop 15\n\ts_nop 3" : "+v"(s_acc));
-          if (i < 16) softmax_step_fp8(st, i, s_acc, mk1 != 0, pb_new);
+          if ((i & 1) == 0) softmax_step_fp8(st, i >> 1, s_acc, mk1 != 0, pb_new);   // steps 0..15
           if (i == 29) {
             // Start of iteration s+1, while PV MFMAs 29..31 (operands in registers) still run:
             // every V read of this iteration is complete, idx(s+5) and the gather of s+3 (issued

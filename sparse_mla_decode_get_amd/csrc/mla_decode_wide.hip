@@ -149,6 +149,7 @@ __device__ __forceinline__ void mfma_pv(f32x16& o, const bf16x8& v, const bf16x8
 
 typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4_w;   // read/write view
 __device__ __forceinline__ bf16x8 lds_k(uint32_t a) {
   return __builtin_bit_cast(bf16x8, *(lds_u32x4*)(uintptr_t)a);
 }
@@ -1039,41 +1040,72 @@ void sparse_decode_wide_kernel(DecodeParams p) {
     }
 
     // ---- epilogue of this row segment. O^T block d: lane l holds head l%32 and dims
-    // 32d + 8(r/4) + 4(l/32) + r%4. Blocks are written one at a time.
+    // 32d + 8(r/4) + 4(l/32) + r%4.
     {
       const int lane = lane_id();
       const int g = lane >> 5;
-      const int head = head_base + (lane & 31);
+      const int h = lane & 31;
+      const int head = head_base + h;
       const bool final_out = nsplit == 1;
-      if (head < p.h_q) {
-        const float inv = l_sum > 0.0f ? 1.0f / l_sum : 0.0f;
+      const float inv = l_sum > 0.0f ? 1.0f / l_sum : 0.0f;
+      if (final_out) {
+        // Final rows in bf16, staged through LDS so that every store writes one head's 1 KB row:
+        // the wave's 32 rows go to its own 32 KB (the tiles and the start of the raw slots, free
+        // after the pass), 8-byte unit u of row h at unit u ^ h (free of bank conflicts both
+        // when written by head and when read along a row).
+        char* const stage = smem + wave * kTileBytes;
+#pragma unroll
+        for (int d = 0; d < 16; ++d) {
+#pragma unroll
+          for (int jb = 0; jb < 4; ++jb) {
+            bf16x4 o;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[i] = (__bf16)(oacc[d][4 * jb + i] * inv);
+            *reinterpret_cast<lds_bf16x4_w*>(lds_addr(stage + h * kTileStride + 8 * ((8 * d + 2 * jb + g) ^ h))) = o;
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        // row r: lane l moves dims 8l .. 8l+7 (units 2l, 2l+1)
+        for (int r = 0; r < 32 && head_base + r < p.h_q; ++r) {
+          const char* src = stage + r * kTileStride;
+          const bf16x4 lo = *reinterpret_cast<const lds_bf16x4_w*>(lds_addr(src + 8 * ((2 * lane) ^ r)));
+          const bf16x4 hi = *reinterpret_cast<const lds_bf16x4_w*>(lds_addr(src + 8 * ((2 * lane + 1) ^ r)));
+          *reinterpret_cast<bf16x8*>(p.out + ((int64_t)row * p.h_q + head_base + r) * kHeadDim + 8 * lane) =
+              __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+        // The staging overwrote the start of the raw slots, which the next segment's first
+        // iterations dequantize before any gather fills them: zero them again once every wave has
+        // read its rows back.
+        // (the pipeline with fp4 records dequantizes gathered slots only)
+        if constexpr (!EXTRA) {
+          wait_and_barrier(0);
+          u32x4 zero = {};
+          const int o0 = (64 * wave + lane_id()) * 16;
+          asm volatile("" : "+v"(zero));               // materialized here, not kept from the start
+          for (int o = o0; o < kWaves * kTileBytes - kOffRaw; o += 64 * kWaves * 16)
+            lds_write16(raws + o, zero);
+        }
+      } else if (head < p.h_q) {
 #pragma unroll
         for (int d = 0; d < 16; ++d) {
 #pragma unroll
           for (int jb = 0; jb < 4; ++jb) {
             const int dim = 32 * d + 8 * jb + 4 * g;
-            if (final_out) {
-              bf16x4 o;
+            f32x4 o;
 #pragma unroll
-              for (int i = 0; i < 4; ++i) o[i] = (__bf16)(oacc[d][4 * jb + i] * inv);
-              *reinterpret_cast<bf16x4*>(p.out + ((int64_t)row * p.h_q + head) * kHeadDim + dim) = o;
-            } else {
-              f32x4 o;
-#pragma unroll
-              for (int i = 0; i < 4; ++i) o[i] = oacc[d][4 * jb + i] * inv;
-              *reinterpret_cast<f32x4*>(p.part_o + ((int64_t)slot * p.h_q + head) * kHeadDim + dim) = o;
-            }
+            for (int i = 0; i < 4; ++i) o[i] = oacc[d][4 * jb + i] * inv;
+            *reinterpret_cast<f32x4*>(p.part_o + ((int64_t)slot * p.h_q + head) * kHeadDim + dim) = o;
           }
           __builtin_amdgcn_sched_barrier(0);
         }
-        if (g == 0) {
-          const float lse = l_sum > 0.0f ? (m_ref + __log2f(l_sum)) * 0.69314718055994530942f
-                                         : -__builtin_inff();
-          if (final_out)
-            p.lse[(int64_t)row * p.h_q + head] = lse;
-          else
-            p.part_lse[(int64_t)slot * p.h_q + head] = lse;
-        }
+      }
+      if (g == 0 && head < p.h_q) {
+        const float lse = l_sum > 0.0f ? (m_ref + __log2f(l_sum)) * 0.69314718055994530942f
+                                       : -__builtin_inff();
+        if (final_out)
+          p.lse[(int64_t)row * p.h_q + head] = lse;
+        else
+          p.part_lse[(int64_t)slot * p.h_q + head] = lse;
       }
     }
     ++row;

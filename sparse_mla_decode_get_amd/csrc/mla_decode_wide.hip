@@ -50,19 +50,29 @@ constexpr uint32_t kIgnoredScoreBits = 0xF180u;
 
 constexpr int kWaves = 4;
 constexpr int kGroupHeads = 32 * kWaves;
-// bf16 tile: token row r at r * 1024 bytes; its 16-byte chunk c (dims 8c .. 8c+7) is stored at
-// chunk position c ^ tile_swizzle(r). The swizzle keeps every access pattern of the kernel free of
-// LDS bank conflicts: 16 rows at one chunk (K row reads, dequant writes) hit 16 different 4-bank
-// groups, and so do 4 rows x 4 consecutive chunks (the transposed V reads).
-constexpr int kTileStride = 1024;
-constexpr int kTileBytes = kSubTokens * kTileStride;    // 32768
+// bf16 tile: token row r at r * 1088 bytes (1 KB of data and 64 bytes of padding); its 16-byte
+// chunk c (dims 8c .. 8c+7) is stored at chunk position c ^ tile_xor(r), which only permutes the
+// chunks within aligned groups of four. The padding moves each row by four 4-bank groups and the
+// XOR picks among the four of a group, so every access pattern of the kernel is free of LDS bank
+// conflicts: 16 rows at one chunk (K row reads, dequant writes) hit 16 different 4-bank groups, and
+// so do 4 rows x 4 consecutive chunks (the transposed V reads). Since the XOR leaves the chunk
+// index above bit 1 alone, operand addresses differ from a few per-lane bases by immediates.
+constexpr int kTileStride = 1088;
+constexpr int kTileBytes = kSubTokens * kTileStride;    // 34816
 constexpr int kRawBytes = kFp8Chunks * kSubTokens * 16; // 16896, chunk-major [chunk][token][16 B]
 constexpr int kIdxBytes = kSubTokens * 4;     // one index slot (lanes 0..31 write it)
+// epilogue staging of the bf16 output: 32 rows of 1 KB per wave, from the start of LDS
+constexpr int kStageRow = 1024;
+constexpr int kStageBytes = 32 * kStageRow;
 constexpr int kStages = 3;
 constexpr int kOffRaw = kStages * kTileBytes;
 constexpr int kOffIdx = kOffRaw + kStages * kRawBytes;
 constexpr int kOffFlags = kOffIdx + kWaves * kStages * kIdxBytes;
 constexpr int kLdsBytes = kOffFlags + 16;
+static_assert(kLdsBytes <= 160 * 1024, "LDS of one workgroup");
+static_assert(kWaves * kStageBytes > kOffRaw && kWaves * kStageBytes <= kOffIdx,
+              "the epilogue staging covers the tiles and part of the raw slots only");
+static_assert(16 * kTileStride + 3 * 256 + 8 < 65536, "PV operand offsets fit the DS immediate");
 // Largest allowed excess of a score over its head's probability reference, in log2 units: P stays
 // below 2^64, the sums far inside fp32 range for any cache value in the exactly decodable range.
 constexpr float kRefSlack = 64.0f;
@@ -71,6 +81,10 @@ constexpr float kRefSlack = 64.0f;
 // fp4 = 2 chunk pairs + 1 scale chunk instruction.
 constexpr int kGatherFp8 = 5;
 constexpr int kGatherFp4 = 3;
+// fp8 pipeline: K and V operands are read kAhead MFMAs before use, through rings of kRing
+// registers (an operand register is rewritten two MFMAs after the MFMA that read it)
+constexpr int kAhead = 5;
+constexpr int kRing = kAhead + 2;
 
 __device__ __forceinline__ int lane_id() {
   int l = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
@@ -182,7 +196,7 @@ __device__ __forceinline__ void wait_and_barrier(int n) {
   }
 }
 
-__device__ __forceinline__ int tile_swizzle(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+__device__ __forceinline__ int tile_xor(int r) { return (r >> 2) & 3; }
 
 __device__ __forceinline__ u32x4 lds_read16(const char* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void lds_write16(char* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
@@ -208,7 +222,7 @@ __device__ __forceinline__ SubTile locate(const DecodeParams& p, int t0, int j) 
 
 // QK^T of one sub-tile: S^T[32 tokens x 32 heads] = K[32 x 512] Q^T with 32 chained
 // v_mfma_f32_32x32x16_bf16 steps. Step kk reads this lane's K fragment (token l%32, dims
-// 16kk + 8(l/32) .. +7) at a[kk % 8] + 256 (kk / 8) (swizzled tile, see tile_swizzle). K fragments
+// 16kk + 8(l/32) .. +7) at a[kk % 8] + 256 (kk / 8) (swizzled tile, see tile_xor). K fragments
 // are read four steps ahead into eight rotating registers, so no fragment is overwritten while an
 // MFMA that reads it may still be in flight.
 //
@@ -330,8 +344,8 @@ __device__ __forceinline__ f32x16 qk_chain(const uint32_t (&a)[8], const bf16x8 
 
 // PV of one sub-tile: O^T[512 dims x 32 heads] += V^T P^T as 32 v_mfma_f32_32x32x16_bf16 steps
 // (step i: token half ks = i / 16, dim block d = i % 16). The V^T operand of a step is two
-// transposed LDS reads (ds_read_b64_tr_b16) at a[d % 4] and a[4 + d % 4], plus 16384 ks +
-// 256 (d / 4) (swizzled tile, see tile_swizzle). Reads run three steps ahead through six fixed operand buffers
+// transposed LDS reads (ds_read_b64_tr_b16) at a[d % 4] and a[4 + d % 4], plus 16 kTileStride ks +
+// 256 (d / 4) (swizzled tile, see tile_xor). Reads run three steps ahead through six fixed operand buffers
 // (v232..v255, declared clobbered so that the compiler keeps nothing there); O stays in the
 // accumulation registers. The block starts with 5 wait states (P may have just been written by
 // VALU instructions) and ends with 20 (before O is read outside).
@@ -399,68 +413,68 @@ __device__ __forceinline__ void pv_chain(const uint32_t (&a)[8], f32x16 (&o)[16]
       "ds_read_b64_tr_b16 v[246:247], %[v7] offset:768\n\t"
       "s_waitcnt lgkmcnt(4)\n\t"
       "v_mfma_f32_32x32x16_bf16 %[o13], v[236:239], %[p0], %[o13]\n\t"
-      "ds_read_b64_tr_b16 v[248:249], %[v0] offset:16384\n\t"
-      "ds_read_b64_tr_b16 v[250:251], %[v4] offset:16384\n\t"
+      "ds_read_b64_tr_b16 v[248:249], %[v0] offset:17408\n\t"
+      "ds_read_b64_tr_b16 v[250:251], %[v4] offset:17408\n\t"
       "s_waitcnt lgkmcnt(4)\n\t"
       "v_mfma_f32_32x32x16_bf16 %[o14], v[240:243], %[p0], %[o14]\n\t"
-      "ds_read_b64_tr_b16 v[252:253], %[v1] offset:16384\n\t"
-      "ds_read_b64_tr_b16 v[254:255], %[v5] offset:16384\n\t"
+      "ds_read_b64_tr_b16 v[252:253], %[v1] offset:17408\n\t"
+      "ds_read_b64_tr_b16 v[254:255], %[v5] offset:17408\n\t"
       "s_waitcnt lgkmcnt(4)\n\t"
       "v_mfma_f32_32x32x16_bf16 %[o15], v[244:247], %[p0], %[o15]\n\t"
-      "ds_read_b64_tr_b16 v[232:233], %[v2] offset:16384\n\t"
-      "ds_read_b64_tr_b16 v[234:235], %[v6] offset:16384\n\t"
+      "ds_read_b64_tr_b16 v[232:233], %[v2] offset:17408\n\t"
+      "ds_read_b64_tr_b16 v[234:235], %[v6] offset:17408\n\t"
       "s_waitcnt lgkmcnt(4)\n\t"
       "v_mfma_f32_32x32x16_bf16 %[o0], v[248:251], %[p1], %[o0]\n\t"
-      "ds_read_b64_tr_b16 v[236:237], %[v3] offset:16384\n\t"
-      "ds_read_b64_tr_b16 v[238:239], %[v7] offset:16384\n\t"
+      "ds_read_b64_tr_b16 v[236:237], %[v3] offset:17408\n\t"
+      "ds_read_b64_tr_b16 v[238:239], %[v7] offset:17408\n\t"
       "s_waitcnt lgkmcnt(4)\n\t"
       "v_mfma_f32_32x32x16_bf16 %[o1], v[252:255], %[p1], %[o1]\n\t"
-      "ds_read_b64_tr_b16 v[240:241], %[v0] offset:16640\n\t"
-      "ds_read_b64_tr_b16 v[242:243], %[v4] offset:16640\n\t"
+      "ds_read_b64_tr_b16 v[240:241], %[v0] offset:17664\n\t"
+      "ds_read_b64_tr_b16 v[242:243], %[v4] offset:17664\n\t"
       "s_waitcnt lgkmcnt(4)\n\t"
       "v_mfma_f32_32x32x16_bf16 %[o2], v[232:235], %[p1], %[o2]\n\t"
-      "ds_read_b64_tr_b16 v[244:245], %[v1] offset:16640\n\t"
-      "ds_read_b64_tr_b16 v[246:247], %[v5] offset:16640\n\t"
+      "ds_read_b64_tr_b16 v[244:245], %[v1] offset:17664\n\t"
+      "ds_read_b64_tr_b16 v[246:247], %[v5] offset:17664\n\t"
       "s_waitcnt lgkmcnt(4)\n\t"
       "v_mfma_f32_32x32x16_bf16 %[o3], v[236:239], %[p1], %[o3]\n\t"
-      "ds_read_b64_tr_b16 v[248:249], %[v2] offset:16640\n\t"
-      "ds_read_b64_tr_b16 v[250:251], %[v6] offset:16640\n\t"
+      "ds_read_b64_tr_b16 v[248:249], %[v2] offset:17664\n\t"
+      "ds_read_b64_tr_b16 v[250:251], %[v6] offset:17664\n\t"
       "s_waitcnt lgkmcnt(4)\n\t"
       "v_mfma_f32_32x32x16_bf16 %[o4], v[240:243], %[p1], %[o4]\n\t"
-      "ds_read_b64_tr_b16 v[252:253], %[v3] offset:16640\n\t"
-      "ds_read_b64_tr_b16 v[254:255], %[v7] offset:16640\n\t"
+      "ds_read_b64_tr_b16 v[252:253], %[v3] offset:17664\n\t"
+      "ds_read_b64_tr_b16 v[254:255], %[v7] offset:17664\n\t"
       "s_waitcnt lgkmcnt(4)\n\t"
       "v_mfma_f32_32x32x16_bf16 %[o5], v[244:247], %[p1], %[o5]\n\t"
-      "ds_read_b64_tr_b16 v[232:233], %[v0] offset:16896\n\t"
-      "ds_read_b64_tr_b16 v[234:235], %[v4] offset:16896\n\t"
+      "ds_read_b64_tr_b16 v[232:233], %[v0] offset:17920\n\t"
+      "ds_read_b64_tr_b16 v[234:235], %[v4] offset:17920\n\t"
       "s_waitcnt lgkmcnt(4)\n\t"
       "v_mfma_f32_32x32x16_bf16 %[o6], v[248:251], %[p1], %[o6]\n\t"
-      "ds_read_b64_tr_b16 v[236:237], %[v1] offset:16896\n\t"
-      "ds_read_b64_tr_b16 v[238:239], %[v5] offset:16896\n\t"
+      "ds_read_b64_tr_b16 v[236:237], %[v1] offset:17920\n\t"
+      "ds_read_b64_tr_b16 v[238:239], %[v5] offset:17920\n\t"
       "s_waitcnt lgkmcnt(4)\n\t"
       "v_mfma_f32_32x32x16_bf16 %[o7], v[252:255], %[p1], %[o7]\n\t"
-      "ds_read_b64_tr_b16 v[240:241], %[v2] offset:16896\n\t"
-      "ds_read_b64_tr_b16 v[242:243], %[v6] offset:16896\n\t"
+      "ds_read_b64_tr_b16 v[240:241], %[v2] offset:17920\n\t"
+      "ds_read_b64_tr_b16 v[242:243], %[v6] offset:17920\n\t"
       "s_waitcnt lgkmcnt(4)\n\t"
       "v_mfma_f32_32x32x16_bf16 %[o8], v[232:235], %[p1], %[o8]\n\t"
-      "ds_read_b64_tr_b16 v[244:245], %[v3] offset:16896\n\t"
-      "ds_read_b64_tr_b16 v[246:247], %[v7] offset:16896\n\t"
+      "ds_read_b64_tr_b16 v[244:245], %[v3] offset:17920\n\t"
+      "ds_read_b64_tr_b16 v[246:247], %[v7] offset:17920\n\t"
       "s_waitcnt lgkmcnt(4)\n\t"
       "v_mfma_f32_32x32x16_bf16 %[o9], v[236:239], %[p1], %[o9]\n\t"
-      "ds_read_b64_tr_b16 v[248:249], %[v0] offset:17152\n\t"
-      "ds_read_b64_tr_b16 v[250:251], %[v4] offset:17152\n\t"
+      "ds_read_b64_tr_b16 v[248:249], %[v0] offset:18176\n\t"
+      "ds_read_b64_tr_b16 v[250:251], %[v4] offset:18176\n\t"
       "s_waitcnt lgkmcnt(4)\n\t"
       "v_mfma_f32_32x32x16_bf16 %[o10], v[240:243], %[p1], %[o10]\n\t"
-      "ds_read_b64_tr_b16 v[252:253], %[v1] offset:17152\n\t"
-      "ds_read_b64_tr_b16 v[254:255], %[v5] offset:17152\n\t"
+      "ds_read_b64_tr_b16 v[252:253], %[v1] offset:18176\n\t"
+      "ds_read_b64_tr_b16 v[254:255], %[v5] offset:18176\n\t"
       "s_waitcnt lgkmcnt(4)\n\t"
       "v_mfma_f32_32x32x16_bf16 %[o11], v[244:247], %[p1], %[o11]\n\t"
-      "ds_read_b64_tr_b16 v[232:233], %[v2] offset:17152\n\t"
-      "ds_read_b64_tr_b16 v[234:235], %[v6] offset:17152\n\t"
+      "ds_read_b64_tr_b16 v[232:233], %[v2] offset:18176\n\t"
+      "ds_read_b64_tr_b16 v[234:235], %[v6] offset:18176\n\t"
       "s_waitcnt lgkmcnt(4)\n\t"
       "v_mfma_f32_32x32x16_bf16 %[o12], v[248:251], %[p1], %[o12]\n\t"
-      "ds_read_b64_tr_b16 v[236:237], %[v3] offset:17152\n\t"
-      "ds_read_b64_tr_b16 v[238:239], %[v7] offset:17152\n\t"
+      "ds_read_b64_tr_b16 v[236:237], %[v3] offset:18176\n\t"
+      "ds_read_b64_tr_b16 v[238:239], %[v7] offset:18176\n\t"
       "s_waitcnt lgkmcnt(4)\n\t"
       "v_mfma_f32_32x32x16_bf16 %[o13], v[252:255], %[p1], %[o13]\n\t"
       "s_waitcnt lgkmcnt(2)\n\t"
@@ -593,7 +607,7 @@ void sparse_decode_wide_kernel(DecodeParams p) {
       const bool valid = (mask >> t) & 1u;
       const char* raw = raws + (j % 3) * kRawBytes;
       char* trow = tiles + (j % 3) * kTileBytes + t * kTileStride;
-      const int sw = tile_swizzle(t);
+      const int sw = tile_xor(t);
       auto chunk = [&](int c) { return trow + 16 * (c ^ sw); };   // bf16 chunk c of this token
       if (!st.fp4) {
         const int c0 = 8 * wave + 4 * g;                     // first of this lane's 4 fp8 chunks
@@ -633,27 +647,27 @@ void sparse_decode_wide_kernel(DecodeParams p) {
     auto is_fp8 = [&](int j) -> bool { return !locate<EXTRA>(p, t0, j).fp4; };
 
     // Per-lane LDS addresses in tile slot 0 (add slot * kTileBytes).
-    // QK^T step kk reads token row l%32, logical chunk 2kk + l/32: with s = tile_swizzle(row) that is
-    // physical chunk 2(kk ^ (s >> 1)) + ((l/32) ^ (s & 1)), i.e. k_addr[kk % 8] + 256 (kk / 8).
+    // QK^T step kk reads token row r = l%32, logical chunk 2kk + g (g = l/32), physical chunk
+    // 4 (kk / 2) + ((2 (kk % 2) + g) ^ tile_xor(r)), i.e. k_addr[kk % 8] + 256 (kk / 8).
     // PV step (ks, d) reads, for h = 0, 1, token row 16ks + 8((l/16)/2) + 4h + (l%16)/4 and logical
-    // chunk 4d + 2((l/16)%2) + (l%4)/2 (8-byte half l%2), i.e. v_addr[4h + d%4] + 16384 ks +
-    // 256 (d / 4).
+    // chunk 4d + 2((l/16)%2) + (l%4)/2 (8-byte half l%2), i.e. v_addr[4h + d%4] + 16 kTileStride ks
+    // + 256 (d / 4).
     uint32_t k_addr[8], v_addr[8];
     {
       const int lane = lane_id();
-      const int r = lane & 31, g = lane >> 5, s = tile_swizzle(r);
+      const int r = lane & 31, g = lane >> 5, x = tile_xor(r);
 #pragma unroll
       for (int j = 0; j < 8; ++j)
-        k_addr[j] = lds_addr(tiles + r * kTileStride + 32 * (j ^ (s >> 1)) + 16 * (g ^ (s & 1)));
+        k_addr[j] = lds_addr(tiles + r * kTileStride + 64 * (j >> 1) + 16 * ((2 * (j & 1) + g) ^ x));
       const int g2 = lane >> 4, jj = lane & 15;
       const int c_lo = 2 * (g2 & 1) + ((jj & 3) >> 1);
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int rw = 8 * (g2 >> 1) + 4 * h + (jj >> 2);
-        const int sr = tile_swizzle(rw);
+        const int xr = tile_xor(rw);
 #pragma unroll
         for (int dd = 0; dd < 4; ++dd)
-          v_addr[4 * h + dd] = lds_addr(tiles + rw * kTileStride + 16 * ((4 * dd + c_lo) ^ sr) + 8 * (jj & 1));
+          v_addr[4 * h + dd] = lds_addr(tiles + rw * kTileStride + 16 * (4 * dd + (c_lo ^ xr)) + 8 * (jj & 1));
       }
     }
     auto slot_addr = [&](const uint32_t (&base)[8], int sl, uint32_t (&out)[8]) {
@@ -826,9 +840,9 @@ void sparse_decode_wide_kernel(DecodeParams p) {
       // Validity masks of sub-tiles s .. s+4 (scalar ring) and the P^T operand of sub-tile s.
       uint32_t mk0 = 0, mk1 = 0, mk2 = 0, mk3 = 0, mk4 = 0;
       bf16x8 pb_cur[2] = {bf16x8{}, bf16x8{}};
-      // K operand ring of the fp8 pipeline; between iterations kb[0..2] hold the first three
+      // K operand ring of the fp8 pipeline; between iterations kb[0 .. kAhead-1] hold the first
       // operands of the next QK^T
-      bf16x8 kb[5];
+      bf16x8 kb[kRing];
       // opaque, so that no copy of the loop is specialised for this constant
       asm volatile("" : "+v"(pb_cur[0]), "+v"(pb_cur[1]));
 
@@ -844,10 +858,15 @@ void sparse_decode_wide_kernel(DecodeParams p) {
         const int t = lane & 31, hh = lane >> 5;
         // operand addresses: K of sub-tile s+1 (phase A), V of sub-tile s (phase B); kb[0..2]
         // already hold the first three K operands
-        uint32_t ka[8], va[8];
-        slot_addr(k_addr, r1, ka);
-        slot_addr(v_addr, r0, va);
-        bf16x8 vb[5];
+        // K of step kk at ka[kk % 2] + 64 (kk / 2), V of PV step n at va[h] + 16 kTileStride (n / 16)
+        // + 64 (n % 16), h = 0, 1
+        const uint32_t ka[2] = {k_addr[0] + r1 * kTileBytes, k_addr[1] + r1 * kTileBytes};
+        const uint32_t va[2] = {v_addr[0] + r0 * kTileBytes, v_addr[4] + r0 * kTileBytes};
+        auto read_v = [&](int n) {
+          const uint32_t off = 16 * kTileStride * (n >> 4) + 64 * (n & 15);
+          return lds_v(va[0] + off, va[1] + off);
+        };
+        bf16x8 vb[kRing];
         f32x16 s_acc;
         // A operand of the extra k-step: lane l (token l%32, dims 8(l/32) ..) holds bf16 1.0 in
         // dim 1 if token l%32 of sub-tile s+1 is ignored (lanes 0..31 only)
@@ -857,7 +876,7 @@ void sparse_decode_wide_kernel(DecodeParams p) {
         // dequantization of s+2: this lane's 4 chunks of 16 values
         const char* draw = raws + r2 * kRawBytes;
         char* trow = tiles + r2 * kTileBytes + t * kTileStride;
-        const int sw = tile_swizzle(t);
+        const int sw = tile_xor(t);
         const int c0 = 8 * wave + 4 * hh;
         uint32_t sc2 = 0;
         u32x4 rr[4];
@@ -872,11 +891,16 @@ void sparse_decode_wide_kernel(DecodeParams p) {
         const uint8_t* gdat = nullptr;
 #pragma unroll
         for (int i = 0; i < 32; ++i) {
-          // operands are read three MFMAs ahead, into phase B's first V operands at the end
-          if (i + 3 < 32) kb[(i + 3) % 5] = lds_k(ka[(i + 3) & 7] + 256 * ((i + 3) >> 3));
-          else vb[i - 29] = lds_v(va[i - 29], va[4 + i - 29]);
+          // operands are read kAhead MFMAs ahead, into phase B's first V operands at the end
+          if (i + kAhead < 32) {
+            const int kk = i + kAhead;
+            kb[kk % kRing] = lds_k(ka[kk & 1] + 64 * (kk >> 1));
+          } else {
+            const int n = i + kAhead - 32;                  // phase B's first V operands
+            vb[n % kRing] = read_v(n);
+          }
           if (i == 0) mfma_qk_first(s_acc, kb[0], qreg[0]);
-          else mfma_qk(s_acc, kb[i % 5], qreg[i]);
+          else mfma_qk(s_acc, kb[i % kRing], qreg[i]);
           // extra k-step after the last one: the ignored score for ignored tokens of s+1, +0 for
           // the others (its operands are built two steps earlier)
           if (i == 31) mfma_qk(s_acc, kflag, qflag);
@@ -945,24 +969,23 @@ void sparse_decode_wide_kernel(DecodeParams p) {
         SoftmaxTemps st;
 #pragma unroll
         for (int i = 0; i < 32; ++i) {
-          if (i + 3 < 32) {
-            const int n = i + 3, nks = n >> 4, nd = n & 15;
-            const uint32_t off = 16384 * nks + 256 * (nd >> 2);
-            vb[n % 5] = lds_v(va[nd & 3] + off, va[4 + (nd & 3)] + off);
-          }
-          mfma_pv(oacc[i & 15], vb[i % 5], pb_cur[i >> 4]);
+          if (i + kAhead < 32) vb[(i + kAhead) % kRing] = read_v(i + kAhead);
+          mfma_pv(oacc[i & 15], vb[i % kRing], pb_cur[i >> 4]);
           // the scores are read by VALU instructions next: 20 wait states after the last QK^T
           // MFMA (the PV MFMA above runs meanwhile)
           if (i == 0) asm volatile("s_nop 15\n\ts_nop 3" : "+v"(s_acc));
           if ((i & 1) == 0) softmax_step_fp8(st, i >> 1, s_acc, mk1 != 0, pb_new);   // steps 0..15
-          if (i == 29) {
-            // Start of iteration s+1, while PV MFMAs 29..31 (operands in registers) still run:
+          if (i == 32 - kAhead) {
+            // Start of iteration s+1, while the last PV MFMAs (operands already read) still run:
             // every V read of this iteration is complete, idx(s+5) and the gather of s+3 (issued
             // in iteration s-1) have landed and all waves' dequantization of s+2 is written, so
             // the first K operands of QK^T(s+2) can be read.
             wait_and_barrier(1 + kGatherFp8);
           }
-          if (i >= 29) kb[i - 29] = lds_k(k_addr[i - 29] + r2 * kTileBytes);
+          if (i >= 32 - kAhead) {
+            const int kk = i - (32 - kAhead);
+            kb[kk] = lds_k(k_addr[kk & 1] + r2 * kTileBytes + 64 * (kk >> 1));
+          }
           __builtin_amdgcn_sched_barrier(0);
         }
         pb_cur[0] = pb_new[0];
@@ -975,7 +998,8 @@ void sparse_decode_wide_kernel(DecodeParams p) {
         // start of iteration -4: idx(0) has landed ("iteration -5" issued only idx(1))
         wait_and_barrier(1);
 #pragma unroll
-        for (int n = 0; n < 3; ++n) kb[n] = lds_k(k_addr[n] + ((-4 + 7) % 3) * kTileBytes);
+        for (int kk = 0; kk < kAhead; ++kk)
+          kb[kk] = lds_k(k_addr[kk & 1] + ((-4 + 7) % 3) * kTileBytes + 64 * (kk >> 1));
       }
 
       // slots of sub-tiles s, s+1, s+2 (s % 3 ... for s >= -4), rotated every iteration
@@ -1053,7 +1077,7 @@ void sparse_decode_wide_kernel(DecodeParams p) {
         // the wave's 32 rows go to its own 32 KB (the tiles and the start of the raw slots, free
         // after the pass), 8-byte unit u of row h at unit u ^ h (free of bank conflicts both
         // when written by head and when read along a row).
-        char* const stage = smem + wave * kTileBytes;
+        char* const stage = smem + wave * kStageBytes;
 #pragma unroll
         for (int d = 0; d < 16; ++d) {
 #pragma unroll
@@ -1061,13 +1085,13 @@ void sparse_decode_wide_kernel(DecodeParams p) {
             bf16x4 o;
 #pragma unroll
             for (int i = 0; i < 4; ++i) o[i] = (__bf16)(oacc[d][4 * jb + i] * inv);
-            *reinterpret_cast<lds_bf16x4_w*>(lds_addr(stage + h * kTileStride + 8 * ((8 * d + 2 * jb + g) ^ h))) = o;
+            *reinterpret_cast<lds_bf16x4_w*>(lds_addr(stage + h * kStageRow + 8 * ((8 * d + 2 * jb + g) ^ h))) = o;
           }
           __builtin_amdgcn_sched_barrier(0);
         }
         // row r: lane l moves dims 8l .. 8l+7 (units 2l, 2l+1)
         for (int r = 0; r < 32 && head_base + r < p.h_q; ++r) {
-          const char* src = stage + r * kTileStride;
+          const char* src = stage + r * kStageRow;
           const bf16x4 lo = *reinterpret_cast<const lds_bf16x4_w*>(lds_addr(src + 8 * ((2 * lane) ^ r)));
           const bf16x4 hi = *reinterpret_cast<const lds_bf16x4_w*>(lds_addr(src + 8 * ((2 * lane + 1) ^ r)));
           *reinterpret_cast<bf16x8*>(p.out + ((int64_t)row * p.h_q + head_base + r) * kHeadDim + 8 * lane) =
@@ -1082,7 +1106,7 @@ void sparse_decode_wide_kernel(DecodeParams p) {
           u32x4 zero = {};
           const int o0 = (64 * wave + lane_id()) * 16;
           asm volatile("" : "+v"(zero));               // materialized here, not kept from the start
-          for (int o = o0; o < kWaves * kTileBytes - kOffRaw; o += 64 * kWaves * 16)
+          for (int o = o0; o < kWaves * kStageBytes - kOffRaw; o += 64 * kWaves * 16)
             lds_write16(raws + o, zero);
         }
       } else if (head < p.h_q) {

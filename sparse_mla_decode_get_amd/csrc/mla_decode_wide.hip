@@ -70,8 +70,7 @@ constexpr int kOffIdx = kOffRaw + kStages * kRawBytes;
 constexpr int kOffFlags = kOffIdx + kWaves * kStages * kIdxBytes;
 constexpr int kLdsBytes = kOffFlags + 16;
 static_assert(kLdsBytes <= 160 * 1024, "LDS of one workgroup");
-static_assert(kWaves * kStageBytes > kOffRaw && kWaves * kStageBytes <= kOffIdx,
-              "the epilogue staging covers the tiles and part of the raw slots only");
+static_assert(kWaves * kStageBytes <= kOffIdx, "the epilogue staging leaves the index ring alone");
 static_assert(16 * kTileStride + 3 * 256 + 8 < 65536, "PV operand offsets fit the DS immediate");
 // Largest allowed excess of a score over its head's probability reference, in log2 units: P stays
 // below 2^64, the sums far inside fp32 range for any cache value in the exactly decodable range.
@@ -504,12 +503,10 @@ void sparse_decode_wide_kernel(DecodeParams p) {
   const uint64_t scale_lanes_fp4 = scale_lanes_fp8 | (scale_lanes_fp8 << 32);
 
   if constexpr (!EXTRA) {
-    // The fp8 pipeline's first iterations read tile slots no sub-tile has been written to yet,
-    // and dequantize raw slots no gather has filled yet (sub-tiles -2 and -1, with zero
-    // probabilities). Zeros in both keep those scores and products finite: the ignored-token score
-    // masks a finite score, not a NaN. Later segments find finite data of earlier sub-tiles there.
-    static_assert(kOffRaw == kStages * kTileBytes, "raw slots follow the tiles");
-    for (int o = threadIdx.x * 16; o < kOffRaw + kStages * kRawBytes; o += 64 * kWaves * 16)
+    // The fp8 pipeline's first full iteration (-1) runs PV on a tile slot no sub-tile has been
+    // written to yet, with zero probabilities: zeros keep those products finite. Later segments
+    // find finite data there (earlier sub-tiles, or the staged bf16 output).
+    for (int o = threadIdx.x * 16; o < kStages * kTileBytes; o += 64 * kWaves * 16)
       lds_write16(tiles + o, u32x4{});
     __syncthreads();
   }
@@ -992,20 +989,84 @@ void sparse_decode_wide_kernel(DecodeParams p) {
         pb_cur[1] = pb_new[1];
       };
 
+
+      // Iterations -4 .. -2 of the fp8 pipeline have no real QK^T or PV yet: they only gather
+      // sub-tiles 0 .. 2, load indices 2 .. 4 and (iteration -2) dequantize sub-tile 0, each ending
+      // in the same wait and barrier as a full iteration (which also issues one index load and
+      // kGatherFp8 copies), so their length is set by memory latency, not by 65 idle MFMAs.
+      auto fp8_prologue_iteration = [&](int s, int r0, int r1, int r2) {
+        const int lane = lane_id();
+        const int t = lane & 31, hh = lane >> 5;
+        const bool g_live = s + 4 < nsub && p.topk > 0;
+        const int g_pos0 = kUnitTokens * t0 + kSubTokens * (s + 4);
+        const char* gidx = idx_ring + r1 * kIdxBytes;
+        const uint32_t graw = __builtin_amdgcn_readfirstlane(lds_addr(raws + r1 * kRawBytes));
+        const int gv = *reinterpret_cast<const int*>(gidx + 4 * t);
+        const bool valid = g_live && g_pos0 + t < p.topk && gv >= 0;
+        mk4 = (uint32_t)__ballot(valid);
+        const uint8_t* grec = valid ? p.kc + (int64_t)gv * kFp8Rec : g_zero.bytes;
+        const uint8_t* gdat = grec + 32 * wave + 16 * hh;
+        copy16_to_lds_off<0>(gdat, __builtin_amdgcn_readfirstlane(graw + 1024 * wave));
+        copy16_to_lds_off<128>(gdat, __builtin_amdgcn_readfirstlane(graw + 1024 * (wave + 4)));
+        copy16_to_lds_off<256>(gdat, __builtin_amdgcn_readfirstlane(graw + 1024 * (wave + 8)));
+        copy16_to_lds_off<384>(gdat, __builtin_amdgcn_readfirstlane(graw + 1024 * (wave + 12)));
+        copy16_to_lds_masked(grec + 512, __builtin_amdgcn_readfirstlane(graw + 32 * 512), scale_lanes_fp8);
+        {
+          const int j = s + 6;
+          const int32_t* src = p.sched;
+          if (j < nsub && p.topk > 0)
+            src = p.idx + (int64_t)row * p.topk + min(kUnitTokens * t0 + kSubTokens * j + lane, p.topk - 1);
+          copy4_to_lds_masked(src, __builtin_amdgcn_readfirstlane(lds_addr(idx_ring + r0 * kIdxBytes)),
+                              0xFFFFFFFFull);
+        }
+        if (s == -2) {
+          // sub-tile 0, gathered in iteration -4 (landed: the last barrier waited for it)
+          const char* draw = raws + r2 * kRawBytes;
+          char* trow = tiles + r2 * kTileBytes + t * kTileStride;
+          const int sw = tile_xor(t);
+          const int c0 = 8 * wave + 4 * hh;
+          const uint32_t sc2 = *reinterpret_cast<const uint16_t*>(draw + (32 * kSubTokens + t) * 16 + c0 / 2);
+#pragma unroll
+          for (int cc = 0; cc < 4; ++cc) {
+            const u32x4 r = lds_read16(draw + ((c0 + cc) * kSubTokens + t) * 16);
+            const uint32_t sb = (sc2 >> (8 * (cc >> 1))) & 0xFFu;
+            lds_write16(trow + 16 * ((2 * (c0 + cc)) ^ sw), __builtin_bit_cast(u32x4, dequant_fp8_8(r[0], r[1], sb)));
+            lds_write16(trow + 16 * ((2 * (c0 + cc) + 1) ^ sw), __builtin_bit_cast(u32x4, dequant_fp8_8(r[2], r[3], sb)));
+          }
+        }
+        wait_and_barrier(1 + kGatherFp8);
+      };
+
       load_indices(0, 0);                        // "iteration -6"
       load_indices(1, 1);                        // "iteration -5"
-      if constexpr (!EXTRA) {
-        // start of iteration -4: idx(0) has landed ("iteration -5" issued only idx(1))
-        wait_and_barrier(1);
-#pragma unroll
-        for (int kk = 0; kk < kAhead; ++kk)
-          kb[kk] = lds_k(k_addr[kk & 1] + ((-4 + 7) % 3) * kTileBytes + 64 * (kk >> 1));
-      }
 
       // slots of sub-tiles s, s+1, s+2 (s % 3 ... for s >= -4), rotated every iteration
       int r0 = 2, r1 = 0, r2 = 1;
+      int s_first = -4;
+      if constexpr (!EXTRA) {
+        // start of iteration -4: idx(0) has landed ("iteration -5" issued only idx(1))
+        wait_and_barrier(1);
+        for (int s = -4; s < -1; ++s) {
+          fp8_prologue_iteration(s, r0, r1, r2);
+          mk0 = mk1;
+          mk1 = mk2;
+          mk2 = mk3;
+          mk3 = mk4;
+          mk4 = 0;
+          const int r_old = r0;
+          r0 = r1;
+          r1 = r2;
+          r2 = r_old;
+        }
+        // the first K operands of QK^T(0) (tile 0, dequantized in iteration -2)
+#pragma unroll
+        for (int kk = 0; kk < kAhead; ++kk)
+          kb[kk] = lds_k(k_addr[kk & 1] + r1 * kTileBytes + 64 * (kk >> 1));
+        s_first = -1;
+      }
+
 #pragma clang loop unroll(disable)
-      for (int s = -4; s < nsub; ++s) {
+      for (int s = s_first; s < nsub; ++s) {
         // Top of iteration s: idx(s+4) and the gather of sub-tile s+2 (issued in iteration s-2)
         // have landed once only iteration s-1's operations (idx(s+5), gather(s+3)) may still be
         // pending.
@@ -1096,18 +1157,6 @@ void sparse_decode_wide_kernel(DecodeParams p) {
           const bf16x4 hi = *reinterpret_cast<const lds_bf16x4_w*>(lds_addr(src + 8 * ((2 * lane + 1) ^ r)));
           *reinterpret_cast<bf16x8*>(p.out + ((int64_t)row * p.h_q + head_base + r) * kHeadDim + 8 * lane) =
               __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        }
-        // The staging overwrote the start of the raw slots, which the next segment's first
-        // iterations dequantize before any gather fills them: zero them again once every wave has
-        // read its rows back.
-        // (the pipeline with fp4 records dequantizes gathered slots only)
-        if constexpr (!EXTRA) {
-          wait_and_barrier(0);
-          u32x4 zero = {};
-          const int o0 = (64 * wave + lane_id()) * 16;
-          asm volatile("" : "+v"(zero));               // materialized here, not kept from the start
-          for (int o = o0; o < kWaves * kStageBytes - kOffRaw; o += 64 * kWaves * 16)
-            lds_write16(raws + o, zero);
         }
       } else if (head < p.h_q) {
 #pragma unroll

@@ -9,7 +9,12 @@ re-reads the records of the previous one from cache.
 Prints one JSON line: TFLOP/s over valid selected tokens (2 * h_q * (512 + 512) flops per valid
 token and row), KV GB/s, the roofline block for the decode kernel, and the CPU oracle baseline.
 
-  python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--config 2] [--no-cpu-baseline]
+The defaults time 2000 back-to-back steps after 300 warm-up steps: right after an idle period the
+GPU's power management holds the decode kernel about 20% below its sustained rate for roughly the
+first 100 launches (~15 ms), so a short run would measure that transient rather than a decode
+loop's steady state.
+
+  python bench.py [--gpus 1] [--steps 2000] [--warmup 300] [--config 2] [--no-cpu-baseline]
 """
 import argparse
 import hashlib
@@ -87,8 +92,8 @@ def cpu_baseline(w, seconds: float):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--sets", type=int, default=4, help="independent index sets cycled over steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")

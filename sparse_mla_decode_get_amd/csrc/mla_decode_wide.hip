@@ -68,7 +68,8 @@ constexpr int kStages = 3;
 constexpr int kOffRaw = kStages * kTileBytes;
 constexpr int kOffIdx = kOffRaw + kStages * kRawBytes;
 constexpr int kOffFlags = kOffIdx + kWaves * kStages * kIdxBytes;
-constexpr int kLdsBytes = kOffFlags + 16;
+constexpr int kOffScan = kOffFlags + 16;      // per-wave last live sub-tile, two segment buffers
+constexpr int kLdsBytes = kOffScan + 2 * kWaves * 4;
 static_assert(kLdsBytes <= 160 * 1024, "LDS of one workgroup");
 static_assert(kWaves * kStageBytes <= kOffIdx, "the epilogue staging leaves the index ring alone");
 static_assert(16 * kTileStride + 3 * 256 + 8 < 65536, "PV operand offsets fit the DS immediate");
@@ -494,6 +495,7 @@ void sparse_decode_wide_kernel(DecodeParams p) {
   char* const tiles = smem;
   char* const raws = smem + kOffRaw;
   int* const redo_flags = reinterpret_cast<int*>(smem + kOffFlags);
+  int* const scan_slots = reinterpret_cast<int*>(smem + kOffScan);
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int head_base = blockIdx.y * kGroupHeads + 32 * wave;   // this wave's first head
@@ -518,10 +520,55 @@ void sparse_decode_wide_kernel(DecodeParams p) {
   const int end_tile = sc[3];
   const int slot_first = sc[4];
   bool first_seg = true;
+  int seg_parity = 0;
 
   while (row < end_row || (row == end_row && t0 < end_tile)) {
     const int t1 = row < end_row ? p.tiles : end_tile;
-    const int nsub = 2 * (t1 - t0);
+    // ---- live length of the segment. A sub-tile whose 32 entries are all ignored (negative, or
+    // past the end of the index row) contributes nothing, so the segment ends after the last
+    // sub-tile with a valid entry; with no valid entry at all it runs no sub-tile and its output is
+    // the empty softmax (zeros, lse -inf). Sub-tiles of ignored entries before that point are
+    // processed with all their tokens masked. Each thread tests entries tid, tid + 256, ... in
+    // batches of 8 independent loads; the per-wave maxima meet in LDS (one buffer per segment
+    // parity, so a wave already in the next segment never overwrites values still being read).
+    int nsub;
+    {
+      const int nsub_all = 2 * (t1 - t0);
+      // opaque, so that nothing derived from the thread index is hoisted out of the segment loop
+      // and kept live through the pipeline
+      int tid = (int)threadIdx.x;
+      asm volatile("" : "+v"(tid));
+      int last = -1;
+      for (int e0 = 0; e0 < nsub_all * kSubTokens; e0 += 8 * 64 * kWaves) {
+        int v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int e = e0 + 64 * kWaves * u + tid;
+          const int j = e / kSubTokens;
+          v[u] = -1;
+          if (j < nsub_all) {
+            const SubTile st = locate<EXTRA>(p, t0, j);
+            const int pos = st.pos0 + e % kSubTokens;
+            if (pos < st.count) v[u] = (st.fp4 ? p.xidx : p.idx)[(int64_t)row * st.count + pos];
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (v[u] >= 0) last = max(last, (e0 + 64 * kWaves * u + tid) / kSubTokens);
+      }
+      // wave maximum, bit by bit from the top with ballots (uniform, no lane shuffles)
+      int wmax = -1;
+      if (__ballot(last >= 0) != 0) {
+        wmax = 0;
+        for (int b = 31 - __builtin_clz((unsigned)nsub_all); b >= 0; --b)
+          if (__ballot(last >= (wmax | (1 << b))) != 0) wmax |= 1 << b;
+      }
+      int* const slots = scan_slots + kWaves * seg_parity;
+      if (lane_id() == 0) slots[wave] = wmax;
+      __syncthreads();
+      nsub = __builtin_amdgcn_readfirstlane(max(max(slots[0], slots[1]), max(slots[2], slots[3])) + 1);
+      seg_parity ^= 1;
+    }
     const int split_base = p.split_ptr[row];
     const int nsplit = p.split_ptr[row + 1] - split_base;
     const int slot = first_seg ? slot_first : split_base;

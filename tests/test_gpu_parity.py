@@ -160,6 +160,28 @@ def test_decode_split_rows(spec, parts, min_tiles):
     check_rows(out, lse, ref_out, ref_lse, spec.name)
 
 
+@pytest.mark.parametrize("parts", [0, 5, 23])
+def test_decode_trailing_ignored_subtiles(parts):
+    """Rows whose selections end in runs of -1 of every length relative to the 32-token sub-tile
+    (live prefixes of 0, 1, 31, 32, 33, 95, 500 and all 1000 entries), one row with a fully ignored
+    sub-tile inside its live part, under the default schedule and under splits that leave whole
+    segments with no valid entry."""
+    spec = Spec("trailing", 4, 2, 128, 1000, 4096)
+    w = make_workload(spec, seed=31)
+    idx = w["indices"].reshape(8, 1000)
+    for r, n_live in enumerate([0, 1, 31, 32, 33, 95, 500, 1000]):
+        idx[r, n_live:] = -1
+    idx[6, 64:96] = -1                            # a whole sub-tile inside the live part
+    idx[7, 999] = -1                              # the last entry ignored, the rest live
+    out, lse, md = _decode(w, num_parts=parts)
+    if parts:
+        assert md.workspace is not None
+    ref_out, ref_lse = _oracle(w)
+    check_rows(out, lse, ref_out, ref_lse, f"trailing/{parts}")
+    assert torch.all(lse[0, 0] == -math.inf)      # the row with no valid entry
+    assert torch.all(out[0, 0] == 0)
+
+
 def test_scores_growing_past_the_first_subtile():
     """Later tokens carry 2^8-times larger values, so scores grow by far more than 2^64 over the
     first 32 tokens' maximum: the decode must still match (a probability reference taken from the

@@ -524,6 +524,70 @@ void sparse_decode_wide_kernel(DecodeParams p) {
 
   while (row < end_row || (row == end_row && t0 < end_tile)) {
     const int t1 = row < end_row ? p.tiles : end_tile;
+    const int nsub_all = 2 * (t1 - t0);
+    int nsub = nsub_all;                       // the live length once the scan below has run
+
+    // Index load of sub-tile j into this wave's index slot j % 3 (lanes 0..31, one entry each;
+    // entries past the end of the index row are fetched from a clamped address and replaced by
+    // -1 when read). It is issued for every iteration: past the last sub-tile, or for a selection
+    // of size 0 (no index array), it reads from the schedule instead (a valid address).
+    auto load_indices = [&](int j, int slot) {
+      const int lane = lane_id();
+      const int32_t* src_ptr = p.sched;
+      if (j < nsub) {
+        const SubTile st = locate<EXTRA>(p, t0, j);
+        if (st.count > 0)
+          src_ptr = (st.fp4 ? p.xidx : p.idx) + (int64_t)row * st.count + min(st.pos0 + lane, st.count - 1);
+      }
+      copy4_to_lds_masked(src_ptr, __builtin_amdgcn_readfirstlane(lds_addr(idx_ring + slot * kIdxBytes)),
+                          0xFFFFFFFFull);
+    };
+
+    // ---- segment start: the first batch of the live-length scan, the first two index rows of
+    // the pipeline and Q are all issued before anything waits, so their latencies overlap.
+    // opaque, so that nothing derived from the thread index is hoisted out of the segment loop
+    // and kept live through the pipeline
+    int tid = (int)threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    // Entry e of the segment is entry e % 32 of its sub-tile e / 32. The 8 loads of a batch are
+    // unconditional (clamped addresses; an empty selection reads the schedule instead), so they
+    // are all in flight together; entries outside the segment or past the index row count as -1.
+    auto scan_batch = [&](int e0, int (&v)[8]) {
+      bool in[8];
+      const int32_t* src[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int e = e0 + 64 * kWaves * u + tid;
+        const SubTile st = locate<EXTRA>(p, t0, min(e / kSubTokens, nsub_all - 1));
+        const int pos = st.pos0 + e % kSubTokens;
+        in[u] = e / kSubTokens < nsub_all && pos < st.count;
+        src[u] = st.count > 0
+                     ? (st.fp4 ? p.xidx : p.idx) + (int64_t)row * st.count + min(pos, st.count - 1)
+                     : p.sched;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = *src[u];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = in[u] ? v[u] : -1;
+    };
+    int scan_v[8];
+    scan_batch(0, scan_v);
+    load_indices(0, 0);                          // "iteration -6" of the first pass
+    load_indices(1, 1);                          // "iteration -5"
+
+    // ---- Q of this wave's 32 heads, B-operand layout of v_mfma_f32_32x32x16_bf16:
+    // lane l holds head l%32, dims 16kk + 8(l/32) .. +7 of k-step kk. Heads past h_q load a copy
+    // of the last head; their results are never stored.
+    bf16x8 qreg[32];
+    {
+      const int lane = lane_id();
+      const int qh = min(head_base + (lane & 31), p.h_q - 1);
+      const u32x4* qp = reinterpret_cast<const u32x4*>(
+          p.q + ((int64_t)row * p.h_q + qh) * kHeadDim + 8 * (lane >> 5));
+#pragma unroll
+      for (int kk = 0; kk < 32; ++kk) qreg[kk] = __builtin_bit_cast(bf16x8, qp[2 * kk]);
+    }
+
     // ---- live length of the segment. A sub-tile whose 32 entries are all ignored (negative, or
     // past the end of the index row) contributes nothing, so the segment ends after the last
     // sub-tile with a valid entry; with no valid entry at all it runs no sub-tile and its output is
@@ -531,26 +595,15 @@ void sparse_decode_wide_kernel(DecodeParams p) {
     // processed with all their tokens masked. Each thread tests entries tid, tid + 256, ... in
     // batches of 8 independent loads; the per-wave maxima meet in LDS (one buffer per segment
     // parity, so a wave already in the next segment never overwrites values still being read).
-    int nsub;
     {
-      const int nsub_all = 2 * (t1 - t0);
-      // opaque, so that nothing derived from the thread index is hoisted out of the segment loop
-      // and kept live through the pipeline
-      int tid = (int)threadIdx.x;
-      asm volatile("" : "+v"(tid));
       int last = -1;
       for (int e0 = 0; e0 < nsub_all * kSubTokens; e0 += 8 * 64 * kWaves) {
         int v[8];
+        if (e0 == 0) {
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int e = e0 + 64 * kWaves * u + tid;
-          const int j = e / kSubTokens;
-          v[u] = -1;
-          if (j < nsub_all) {
-            const SubTile st = locate<EXTRA>(p, t0, j);
-            const int pos = st.pos0 + e % kSubTokens;
-            if (pos < st.count) v[u] = (st.fp4 ? p.xidx : p.idx)[(int64_t)row * st.count + pos];
-          }
+          for (int u = 0; u < 8; ++u) v[u] = scan_v[u];
+        } else {
+          scan_batch(e0, v);
         }
 #pragma unroll
         for (int u = 0; u < 8; ++u)
@@ -573,38 +626,11 @@ void sparse_decode_wide_kernel(DecodeParams p) {
     const int nsplit = p.split_ptr[row + 1] - split_base;
     const int slot = first_seg ? slot_first : split_base;
 
-    // ---- Q of this wave's 32 heads, B-operand layout of v_mfma_f32_32x32x16_bf16:
-    // lane l holds head l%32, dims 16kk + 8(l/32) .. +7 of k-step kk. Heads past h_q load a copy
-    // of the last head; their results are never stored.
-    bf16x8 qreg[32];
-    {
-      const int lane = lane_id();
-      const int qh = min(head_base + (lane & 31), p.h_q - 1);
-      const u32x4* qp = reinterpret_cast<const u32x4*>(
-          p.q + ((int64_t)row * p.h_q + qh) * kHeadDim + 8 * (lane >> 5));
-#pragma unroll
-      for (int kk = 0; kk < 32; ++kk) qreg[kk] = __builtin_bit_cast(bf16x8, qp[2 * kk]);
-    }
-    // Q is resident before any asynchronous copy of this segment is issued, so the compiler's
-    // own wait for it cannot end up waiting for the gathers as well.
+    // Q and the first two index rows are resident before any further asynchronous copy of this
+    // segment is issued, so the compiler's own wait for Q cannot end up waiting for the gathers.
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
 
     // ---- asynchronous stages (see the file comment).
-    // Index load of sub-tile j into this wave's index slot j % 3 (lanes 0..31, one entry each;
-    // entries past the end of the index row are fetched from a clamped address and replaced by
-    // -1 when read). It is issued for every iteration: past the last sub-tile, or for a selection
-    // of size 0 (no index array), it reads from the schedule instead (a valid address).
-    auto load_indices = [&](int j, int slot) {
-      const int lane = lane_id();
-      const int32_t* src_ptr = p.sched;
-      if (j < nsub) {
-        const SubTile st = locate<EXTRA>(p, t0, j);
-        if (st.count > 0)
-          src_ptr = (st.fp4 ? p.xidx : p.idx) + (int64_t)row * st.count + min(st.pos0 + lane, st.count - 1);
-      }
-      copy4_to_lds_masked(src_ptr, __builtin_amdgcn_readfirstlane(lds_addr(idx_ring + slot * kIdxBytes)),
-                          0xFFFFFFFFull);
-    };
     // Gather of sub-tile j into raw slot j % 3; returns the validity mask of its 32 tokens.
     // Ignored tokens fetch record 0 (it exists whenever the selection is not empty), so every wave
     // issues a fixed number of copies per sub-tile; their values are never used. A sub-tile of an
@@ -1084,8 +1110,10 @@ void sparse_decode_wide_kernel(DecodeParams p) {
         wait_and_barrier(1 + kGatherFp8);
       };
 
-      load_indices(0, 0);                        // "iteration -6"
-      load_indices(1, 1);                        // "iteration -5"
+      if (pass > 0) {                            // the first pass's were issued with Q
+        load_indices(0, 0);                      // "iteration -6"
+        load_indices(1, 1);                      // "iteration -5"
+      }
 
       // slots of sub-tiles s, s+1, s+2 (s % 3 ... for s >= -4), rotated every iteration
       int r0 = 2, r1 = 0, r2 = 1;

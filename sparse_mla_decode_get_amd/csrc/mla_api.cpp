@@ -26,6 +26,8 @@ bool wide_for(int h_q) { return h_q > 64; }
 int group_heads(int h_q) { return wide_for(h_q) ? 128 : 64; }
 int head_groups(int h_q) { return (h_q + group_heads(h_q) - 1) / group_heads(h_q); }
 
+constexpr int kAutoMinUnits = 4;
+
 int default_parts(int h_q) {
   int dev = 0, cus = 256;
   if (hipGetDevice(&dev) == hipSuccess) {
@@ -55,7 +57,13 @@ int resolve_parts(int batch, int seq_len_q, int h_q, int topk, int extra_topk, i
   int rc = check_shape(batch, seq_len_q, h_q, topk, extra_topk);
   if (rc != MLA_OK) return rc;
   if (num_parts < 0 || min_tiles_per_part < 1 || !out) return MLA_ERR_INVALID_ARG;
-  if (num_parts == 0) num_parts = default_parts(h_q);
+  if (num_parts == 0) {
+    // the default also keeps at least kAutoMinUnits units per part: a part's fixed traffic (its
+    // rows' Q, and a 512-float partial per head when it splits a row) is worth several units of
+    // 64 records
+    num_parts = default_parts(h_q);
+    if (min_tiles_per_part < kAutoMinUnits) min_tiles_per_part = kAutoMinUnits;
+  }
   const int64_t units = (int64_t)batch * seq_len_q * tiles_per_row(topk, extra_topk, nullptr);
   int64_t p = units / min_tiles_per_part;
   if (p > num_parts) p = num_parts;

@@ -20,19 +20,41 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
   const int n = split_ptr[row + 1] - a;
   if (skip_single && n == 1) return;      // written directly by the decode kernel
   const float ninf = -__builtin_inff();
+  const float* lse_col = partial_lse + (int64_t)a * h_q + head;
+  // Splits are taken kBatch at a time with all their loads issued before any is used, so a row
+  // with many splits costs a few memory round trips rather than one per split.
+  constexpr int kBatch = 8;
   float m = ninf;
-  for (int i = 0; i < n; ++i) m = fmaxf(m, partial_lse[(int64_t)(a + i) * h_q + head]);
+  for (int i0 = 0; i0 < n; i0 += kBatch) {
+    float li[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) li[u] = i0 + u < n ? lse_col[(int64_t)(i0 + u) * h_q] : ninf;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) m = fmaxf(m, li[u]);
+  }
   const int dim = 4 * threadIdx.x;
+  const float* o_col = partial + ((int64_t)a * h_q + head) * kHeadDim + dim;
   f32x4 acc = f32x4{};
   float wsum = 0.0f;
   if (m != ninf) {
-    for (int i = 0; i < n; ++i) {
-      const float li = partial_lse[(int64_t)(a + i) * h_q + head];
-      if (li == ninf) continue;
-      const float w = __expf(li - m);
-      wsum += w;
-      const f32x4 o = *reinterpret_cast<const f32x4*>(partial + ((int64_t)(a + i) * h_q + head) * kHeadDim + dim);
-      acc += w * o;
+    for (int i0 = 0; i0 < n; i0 += kBatch) {
+      float li[kBatch];
+      f32x4 o[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const bool in = i0 + u < n;
+        li[u] = in ? lse_col[(int64_t)(i0 + u) * h_q] : ninf;
+        o[u] = in ? *reinterpret_cast<const f32x4*>(o_col + (int64_t)(i0 + u) * h_q * kHeadDim)
+                  : f32x4{};
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        // an empty split (lse -inf) carries no weight, whatever its partial holds
+        if (li[u] == ninf) continue;
+        const float w = __expf(li[u] - m);
+        wsum += w;
+        acc += w * o[u];
+      }
     }
   }
   const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;

@@ -9,27 +9,31 @@
 //
 // Work decomposition. The grid is (parts, head groups). A workgroup takes the contiguous range of
 // (row, 64-slot unit) work the tile-scheduler metadata gives its part, for HG query heads
-// (HG = 64 here) with W = HG / 16 = 4 waves. Every wave has the same register
-// footprint: Q of 16 heads (64 VGPRs) and an fp32 output accumulator of 8 MFMA blocks.
+// (HG = 64 here) with W = HG / 16 = 4 waves, one workgroup per CU. Every wave has the same
+// register footprint: Q of 16 heads (64 VGPRs) and an fp32 output accumulator of 8 MFMA blocks.
 // Each 64-slot unit runs as two sub-tiles of 32 tokens:
-//   1. gather   all lanes copy 16-byte chunks of the selected records (data and scales together,
+//   1. indices  each wave copies the sub-tile's 32 index entries into its LDS index ring
+//               (global_load_lds_dword), 2 * kDepth sub-tiles ahead of the compute.
+//   2. gather   all lanes copy 16-byte chunks of the selected records (data and scales together,
 //               one contiguous record per token) straight from HBM into LDS with
-//               global_load_lds_dwordx4, one sub-tile ahead, chunk-major: slot(chunk c, token t) =
-//               c * 32 + t, so one wave instruction fills a contiguous 1 KB (chunks 2q, 2q+1).
-//   2. QK^T     wave w owns heads 16w..16w+15; each lane reads 16 raw bytes of one token (a
-//               conflict-free ds_read_b128 thanks to the chunk-major layout), dequantizes them in
-//               registers with the record's own scale, and issues v_mfma_f32_16x16x32_bf16 against
-//               its register-resident Q: S^T[16 tokens x 16 heads] over all 512 dims.
-//   3. V slice  while dequantizing, wave w stores the bf16 values of its own PV dim slice
-//               (512 / W dims) to a private LDS area, zeroing ignored tokens.
-//   4. softmax  lanes n, n+16, n+32, n+48 share head n: masked max over the sub-tile, lazy rescale of
+//               global_load_lds_dwordx4, kDepth sub-tiles ahead, chunk-major: slot(chunk c, token t)
+//               = c * 32 + t, so one wave instruction fills a contiguous 1 KB (chunks 2q, 2q+1).
+//               A fixed number of copies per wave and sub-tile lets one s_waitcnt wait for
+//               exactly the oldest sub-tile while the newer ones stay in flight.
+//   3. dequant  wave w converts its 512 / W dims of the 32 tokens to bf16 (the record's own scale,
+//               in registers) into its slice of the LDS tile, zeroing ignored tokens; the W slices
+//               form the sub-tile's bf16 tile, written once and read by every wave.
+//   4. QK^T     wave w owns heads 16w..16w+15: v_mfma_f32_16x16x32_bf16 of tile rows (conflict-free
+//               ds_read_b128) against its register-resident Q, S^T[16 tokens x 16 heads] over all
+//               512 dims.
+//   5. softmax  lanes n, n+16, n+32, n+48 share head n: masked max over the sub-tile, lazy rescale of
 //               the running max (only when it grows by more than 2^8), exp2, bf16 P to LDS, the
 //               running sum of the fp32 probabilities (so lse carries no bf16 rounding), and a
 //               per-wave "rescale needed" flag.
-//   5. PV       wave w accumulates O^T[its dim slice x all HG heads] += V^T P^T with
-//               v_mfma_f32_32x32x16_bf16; V^T comes from its private slice via ds_read_b64_tr_b16,
+//   6. PV       wave w accumulates O^T[its dim slice x all HG heads] += V^T P^T with
+//               v_mfma_f32_32x32x16_bf16; V^T comes from its own tile slice via ds_read_b64_tr_b16,
 //               P^T from LDS.
-//   6. epilogue one split: out = O / l in bf16 and lse = ln(2) * (m + log2 l); several splits: the
+//   7. epilogue one split: out = O / l in bf16 and lse = ln(2) * (m + log2 l); several splits: the
 //               normalised fp32 partial and its lse go to the workspace for the merge kernel.
 
 #include "mla_device.h"
@@ -37,16 +41,23 @@
 
 namespace mla {
 
+// Gather distance in sub-tiles: the records of sub-tile s + kDepth are requested while sub-tile s
+// is computed, and its index entries kDepth sub-tiles before that.
+constexpr int kDepth = 1;
+
 template <int W>
 struct DecodeCfg {
   static constexpr int HG = 16 * W;                 // heads per workgroup
   static constexpr int kThreads = 64 * W;
-  static constexpr int kSlice = kHeadDim / W;       // PV dims per wave
+  static constexpr int kSlice = kHeadDim / W;       // dims per wave (dequant and PV)
   static constexpr int kDB = kSlice / 32;           // 32-dim output blocks per wave
   static constexpr int kHB = HG / 32;               // 32-head output blocks
-  static constexpr int kNQ = (17 + W - 1) / W;      // gather instructions per wave per sub-tile
-  static constexpr int kRawBytes = kFp8Chunks * kSubTokens * 16;   // 16896 per raw buffer
-  static constexpr int kVStride = kSlice * 2 + 16;  // bytes per token row of a V slice
+  static constexpr int kNQ = (17 + W - 1) / W;      // record copies per wave per sub-tile
+  static constexpr int kRawSlots = kDepth + 1;
+  // 34 chunks of 32 tokens: the copy of fp8 chunk pair 16 also writes a (zero) 34th chunk
+  static constexpr int kRawSlotBytes = 34 * kSubTokens * 16;
+  static constexpr int kIdxSlots = kDepth + 1;      // index rows per wave
+  static constexpr int kVStride = kSlice * 2 + 16;  // bytes per token row of a tile slice
   static constexpr int kVBytes = kSubTokens * kVStride;
   static constexpr int kPStride = 80;               // bytes per head row of P (32 bf16 + pad)
   static constexpr int kOffV = 0;
@@ -55,8 +66,16 @@ struct DecodeCfg {
   static constexpr int kOffMFin = kOffAlpha + HG * 4;
   static constexpr int kOffLFin = kOffMFin + HG * 4;
   static constexpr int kOffFlag = kOffLFin + HG * 4;
-  static constexpr int kLdsBytes = kOffFlag + 4 * W;
+  static constexpr int kOffIdx = kOffFlag + 16;
+  static constexpr int kOffDummy = kOffIdx + W * kIdxSlots * kSubTokens * 4;
+  static constexpr int kLdsBytes = kOffDummy + 1024;
+  // the steady-state wait: everything but the copies of the kDepth - 1 newest sub-tiles
+  static constexpr int kVmcntAfterOldest = (kDepth - 1) * (kNQ + 1);
   static_assert(kDB * kHB == 8, "every wave holds 8 output blocks");
+  static_assert(W * kNQ * 2 >= kFp8Chunks, "the copies cover an fp8 record");
+  static_assert(kOffIdx % 16 == 0 && kOffDummy % 16 == 0, "aligned LDS areas");
+  static_assert(kLdsBytes + kRawSlots * kRawSlotBytes <= 160 * 1024, "LDS of one workgroup");
+  static_assert(kVmcntAfterOldest < 64, "vmcnt counts up to 63");
 };
 
 __device__ __forceinline__ u32x4 lds_read16(const char* base, int off) {
@@ -64,19 +83,6 @@ __device__ __forceinline__ u32x4 lds_read16(const char* base, int off) {
 }
 __device__ __forceinline__ void lds_write16(char* base, int off, u32x4 v) {
   *reinterpret_cast<u32x4*>(base + off) = v;
-}
-
-// Index entry of token `tok` of sub-tile `s` in the unit range that starts at unit `t0` of `row`.
-template <bool EXTRA>
-__device__ __forceinline__ int load_index(const DecodeParams& p, int row, int t0, int s, int tok) {
-  const int unit = t0 + (s >> 1);
-  const int half = s & 1;
-  if (!EXTRA || unit < p.tiles_k) {
-    const int pos = unit * kUnitTokens + half * kSubTokens + tok;
-    return pos < p.topk ? p.idx[(int64_t)row * p.topk + pos] : -1;
-  }
-  const int pos = (unit - p.tiles_k) * kUnitTokens + half * kSubTokens + tok;
-  return pos < p.extra_topk ? p.xidx[(int64_t)row * p.extra_topk + pos] : -1;
 }
 
 // Value of lane (lane ^ 16); `lane` is the caller's (opaque) lane id.
@@ -123,6 +129,41 @@ __device__ __forceinline__ void copy16_to_lds(const void* gptr, uint32_t lds_bas
       : "memory");
 }
 
+// One 4-byte global -> LDS copy per lane of the lower half-wave (global_load_lds_dword with EXEC =
+// lanes 0..31): LDS bytes m0 + 4 * lane. Issued with that EXEC inside the assembly, so no branch can
+// skip it; m0 and EXEC are restored.
+__device__ __forceinline__ void copy4_to_lds_lo32(const void* gptr, uint32_t lds_base) {
+  uint32_t saved_m0;
+  uint64_t saved_exec;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b64 %1, exec\n\t"
+      "s_mov_b64 exec, 0xffffffff\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %3, off\n\t"
+      "s_mov_b64 exec, %1\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved_m0), "=&s"(saved_exec)
+      : "s"(lds_base), "v"(gptr)
+      : "memory");
+}
+
+// Waits until only the copies of the kDepth - 1 newest sub-tiles are outstanding in this wave (its
+// copies of the oldest sub-tile and the index row issued right after them have landed) and that all
+// of its LDS accesses are done, then synchronises the workgroup.
+#define MLA_NARROW_VMCNT 0
+static_assert(MLA_NARROW_VMCNT == DecodeCfg<4>::kVmcntAfterOldest, "wait count of the gather pipeline");
+#define MLA_STR2(x) #x
+#define MLA_STR(x) MLA_STR2(x)
+__device__ __forceinline__ void wait_gather_and_barrier() {
+  asm volatile("s_waitcnt vmcnt(" MLA_STR(MLA_NARROW_VMCNT) ") lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Read-only zeros standing in for the records of ignored tokens and for unused copies (an fp8
+// record's 34th chunk included): every gather copy has a valid source.
+__device__ const uint8_t g_zero_record[34 * 16] = {};
+
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
@@ -132,7 +173,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void sparse_decode_kernel(DecodeParams p) {
   using C = DecodeCfg<W>;
   __shared__ __attribute__((aligned(16))) char smem[C::kLdsBytes];
-  __shared__ __attribute__((aligned(16))) char rawbuf[2 * C::kRawBytes];   // double-buffered records
+  __shared__ __attribute__((aligned(16))) char rawbuf[C::kRawSlots * C::kRawSlotBytes];   // gathered records
 
   // The wave index is uniform: keep it (and everything derived from it) in scalar registers.
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -194,118 +235,90 @@ void sparse_decode_kernel(DecodeParams p) {
     float m_run = -__builtin_inff();
     float l_run = 0.0f;
 
-    // ---- gather: direct HBM -> LDS copies of sub-tile s+1 while sub-tile s is computed.
-    // Wave instruction q moves chunks 2q (lanes 0..31) and 2q+1 (lanes 32..63) of the 32 tokens;
-    // lanes whose token is ignored, and lanes past the record, issue nothing.
-    auto issue = [&](int s, int my_idx, char* buf, bool& is_fp4) -> uint32_t {
-      const int unit = t0 + (s >> 1);
-      is_fp4 = EXTRA && unit >= p.tiles_k;
-      const bool valid = my_idx >= 0;
-      const uint32_t bal = (uint32_t)__ballot(valid);   // lanes 0..31 carry tokens 0..31
-      const int nq = is_fp4 ? (kFp4Chunks / 2) : 17;
-      const int nch = is_fp4 ? kFp4Chunks : kFp8Chunks;
-      const uint32_t buf_lds = __builtin_amdgcn_readfirstlane(lds_addr(buf));
-      // per-lane record pointer, already advanced to this lane's chunk of each chunk pair
-      const uint8_t* lane_base = (is_fp4 ? p.xc + (int64_t)(valid ? my_idx : 0) * kFp4Rec
-                                         : p.kc + (int64_t)(valid ? my_idx : 0) * kFp8Rec) + 16 * hh;
+    // ---- asynchronous stages. Sub-tile j's 32 index entries are copied to this wave's index ring
+    // slot j % kIdxSlots, 2 * kDepth sub-tiles ahead of its compute; its records are gathered into
+    // raw slot j % kRawSlots kDepth sub-tiles ahead. Every wave issues exactly kNQ record copies
+    // and one index copy per sub-tile, all with a non-empty EXEC, whatever the sub-tile holds
+    // (ignored tokens, the missing 34th chunk of an fp8 record and an fp4 sub-tile's unused copies
+    // read a zero record; unused copies land in a dummy LDS area), so that one s_waitcnt with a
+    // fixed count waits for exactly the oldest sub-tile.
+    const uint32_t idx_ring = lds_addr(smem + C::kOffIdx + wave * C::kIdxSlots * kSubTokens * 4);
+    auto sub_count = [&](int j, int& pos0, bool& fp4) -> int {   // entries of j's index array
+      const int unit = t0 + (j >> 1);
+      fp4 = EXTRA && unit >= p.tiles_k;
+      if (!fp4) { pos0 = unit * kUnitTokens + (j & 1) * kSubTokens; return p.topk; }
+      pos0 = (unit - p.tiles_k) * kUnitTokens + (j & 1) * kSubTokens;
+      return p.extra_topk;
+    };
+    auto load_idx = [&](int j) {
+      const int32_t* src = p.sched;                  // a valid address when j is past the segment
+      if (j < nsub) {
+        int pos0;
+        bool fp4;
+        const int count = sub_count(j, pos0, fp4);
+        if (count > 0)
+          src = (fp4 ? p.xidx : p.idx) + (int64_t)row * count + min(pos0 + (lane_id() & 31), count - 1);
+      }
+      copy4_to_lds_lo32(src, __builtin_amdgcn_readfirstlane(idx_ring + (j % C::kIdxSlots) * kSubTokens * 4));
+    };
+    // Gather of sub-tile j (its index entries have landed); returns its validity mask.
+    auto gather = [&](int j) -> uint32_t {
+      const int ln = lane_id();
+      const int t = ln & 31, half = ln >> 5;
+      int pos0 = 0;
+      bool fp4 = false;
+      const int count = j < nsub ? sub_count(j, pos0, fp4) : 0;
+      const int v = *reinterpret_cast<const int*>(smem + C::kOffIdx +
+                                                  (wave * C::kIdxSlots + j % C::kIdxSlots) * kSubTokens * 4 + 4 * t);
+      const bool valid = pos0 + t < count && v >= 0;
+      const uint32_t bal = (uint32_t)__ballot(valid);
+      const int nq = fp4 ? kFp4Chunks / 2 : (kFp8Chunks + 1) / 2;
+      const int nch = fp4 ? kFp4Chunks : kFp8Chunks;
+      const uint8_t* rec = !valid ? g_zero_record
+                                  : fp4 ? p.xc + (int64_t)v * kFp4Rec : p.kc + (int64_t)v * kFp8Rec;
+      const uint32_t raw_lds = lds_addr(rawbuf + (j % C::kRawSlots) * C::kRawSlotBytes);
 #pragma unroll
-      for (int j = 0; j < C::kNQ; ++j) {
-        const int qi = wave + W * j;                      // uniform: chunks 2qi (+0) and 2qi+1 (+16)
-        if (qi < nq) {
-          const uint32_t dst = __builtin_amdgcn_readfirstlane(buf_lds + 1024 * qi);
-          const bool ok = valid && (2 * qi + 1 < nch || hh == 0);
-          if (ok) copy16_to_lds(lane_base + 32 * qi, dst);
-        }
+      for (int i = 0; i < C::kNQ; ++i) {
+        const int qi = wave + W * i;                   // uniform: chunks 2qi (+0) and 2qi+1 (+16)
+        const bool used = qi < nq;
+        const uint8_t* src = used && 2 * qi + half < nch ? rec + 32 * qi + 16 * half : g_zero_record;
+        const uint32_t dst = used ? raw_lds + 1024 * qi : lds_addr(smem + C::kOffDummy);
+        copy16_to_lds(src, __builtin_amdgcn_readfirstlane(dst));
       }
       return bal;
     };
 
-    int idx_cur = load_index<EXTRA>(p, row, t0, 0, tok);
-    bool fp4_next = false;
-    uint32_t mask_next = issue(0, idx_cur, rawbuf, fp4_next);
-    int idx_next = nsub > 1 ? load_index<EXTRA>(p, row, t0, 1, tok) : -1;
+    // Prologue: index entries of sub-tiles 0 .. kDepth-1 (waited for together with Q), then the
+    // gathers of those sub-tiles, each followed by the index copy kDepth further on, as in the loop.
+#pragma unroll
+    for (int j = 0; j < kDepth; ++j) load_idx(j);
+    // vmcnt(0) as a compiler-visible wait, so Q counts as resident for the rest of the segment
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    uint32_t mk[kDepth + 1];                          // validity masks of sub-tiles s .. s+kDepth
+#pragma unroll
+    for (int j = 0; j < kDepth; ++j) {
+      mk[j] = gather(j);
+      load_idx(j + kDepth);
+    }
 
     for (int s = 0; s < nsub; ++s) {
-      char* raw = rawbuf + (s & 1) * C::kRawBytes;
-      char* raw_other = rawbuf + ((s + 1) & 1) * C::kRawBytes;
-      const uint32_t mask = mask_next;
-      const bool is_fp4 = EXTRA && fp4_next;
+      const char* raw = rawbuf + (s % C::kRawSlots) * C::kRawSlotBytes;
+      const uint32_t mask = mk[0];
+      int pos0_s;
+      bool is_fp4;
+      sub_count(s, pos0_s, is_fp4);
+      // The gather of s (and the index entries of s + kDepth) have landed for every wave; every wave
+      // is done with the previous sub-tile's tile, P and raw slot.
+      wait_gather_and_barrier();
+      mk[kDepth] = gather(s + kDepth);
+      load_idx(s + 2 * kDepth);
       const int lane = lane_id();
-      const int tok = lane & 31;
-      const int hh = lane >> 5;
       const int t16 = lane & 15;
       const int q4 = lane >> 4;
-      barrier_all();
-      if (s + 1 < nsub) {
-        mask_next = issue(s + 1, idx_next, raw_other, fp4_next);
-        idx_next = (s + 2 < nsub) ? load_index<EXTRA>(p, row, t0, s + 2, tok) : -1;
-      }
+      const int hh = lane >> 5;
       if (mask != 0) {
-        // ---------------- QK^T with in-register dequant (two token blocks, two MFMA chains).
-        // The LDS read of step c+1 is issued before step c is converted; the scheduling barrier
-        // keeps the compiler from hoisting every read of the loop (which would exhaust registers).
-        f32x4 sacc[2] = {f32x4{}, f32x4{}};
-        if (!is_fp4) {
-          u32x4 scl[2], rn[2];
-          const uint32_t sc_shift = 8 * (q4 >> 1);
-#pragma unroll
-          for (int tb = 0; tb < 2; ++tb) {
-            scl[tb] = lds_read16(raw, (32 * kSubTokens + 16 * tb + t16) * 16);   // e8m0 scales
-            rn[tb] = lds_read16(raw, ((0 + q4) * kSubTokens + 16 * tb + t16) * 16);
-          }
-#pragma unroll
-          for (int c = 0; c < 8; ++c) {
-            u32x4 r[2] = {rn[0], rn[1]};
-            if (c + 1 < 8) {
-#pragma unroll
-              for (int tb = 0; tb < 2; ++tb)
-                rn[tb] = lds_read16(raw, ((4 * (c + 1) + q4) * kSubTokens + 16 * tb + t16) * 16);
-            }
-            // 32-dim scale block 2c + q4/2: word c/2 of the 16 scale bytes (a constant index),
-            // byte 2(c&1) + q4/2 inside it (a per-lane shift)
-#pragma unroll
-            for (int tb = 0; tb < 2; ++tb) {
-              const uint32_t sb = __builtin_amdgcn_ubfe(scl[tb][c >> 1], 16 * (c & 1) + sc_shift, 8);
-              bf16x8 a0, a1;
-              dequant_fp8_16(r[tb], sb, a0, a1);
-              sacc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qreg[c][0], sacc[tb], 0, 0, 0);
-              sacc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qreg[c][1], sacc[tb], 0, 0, 0);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-          }
-        } else {
-          u32x2 rn[2];
-#pragma unroll
-          for (int tb = 0; tb < 2; ++tb)
-            rn[tb] = *reinterpret_cast<const u32x2*>(
-                raw + ((q4 >> 1) * kSubTokens + 16 * tb + t16) * 16 + 8 * (q4 & 1));
-#pragma unroll
-          for (int c = 0; c < 8; ++c) {
-            // dims 64c + 16*q4 .. +15 = bytes 32c + 8*q4 .. +7 = chunk 2c + q4/2, offset 8*(q4&1);
-            // their e4m3 scale is byte j % 16 of chunk 16 + j / 16, j = 4c + q4
-            u32x2 r[2] = {rn[0], rn[1]};
-            if (c + 1 < 8) {
-#pragma unroll
-              for (int tb = 0; tb < 2; ++tb)
-                rn[tb] = *reinterpret_cast<const u32x2*>(
-                    raw + ((2 * (c + 1) + (q4 >> 1)) * kSubTokens + 16 * tb + t16) * 16 + 8 * (q4 & 1));
-            }
-            const int j = 4 * c + q4;
-#pragma unroll
-            for (int tb = 0; tb < 2; ++tb) {
-              const uint32_t sb = *reinterpret_cast<const uint8_t*>(
-                  raw + ((16 + (j >> 4)) * kSubTokens + 16 * tb + t16) * 16 + (j & 15));
-              bf16x8 a0, a1;
-              dequant_fp4_16(r[tb][0], r[tb][1], e4m3_to_f32(sb), a0, a1);
-              sacc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qreg[c][0], sacc[tb], 0, 0, 0);
-              sacc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qreg[c][1], sacc[tb], 0, 0, 0);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-          }
-        }
-
-        // ---------------- this wave's PV dim slice of the same tokens, dequantized for the V operand
-        // (zero for ignored tokens) into the wave's private LDS slice, token-major.
+        // ---------------- this wave's dim slice of the sub-tile's 32 tokens, raw -> bf16 tile slice
+        // (zero for ignored tokens); the four slices make up the tile that QK^T and PV read.
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb) {
           const int t = 16 * tb + t16;
@@ -322,14 +335,32 @@ void sparse_decode_kernel(DecodeParams p) {
             } else {
               const u32x2 r = *reinterpret_cast<const u32x2*>(
                   raw + ((2 * c + (q4 >> 1)) * kSubTokens + t) * 16 + 8 * (q4 & 1));
-              const int j = 4 * c + q4;
+              const int jj = 4 * c + q4;
               const uint32_t sb = *reinterpret_cast<const uint8_t*>(
-                  raw + ((16 + (j >> 4)) * kSubTokens + t) * 16 + (j & 15));
+                  raw + ((16 + (jj >> 4)) * kSubTokens + t) * 16 + (jj & 15));
               dequant_fp4_16(r[0], r[1], e4m3_to_f32(sb), a0, a1);
             }
             const int off = t * C::kVStride + (64 * cs + 16 * q4) * 2;
             lds_write16(vslice, off, tok_valid ? __builtin_bit_cast(u32x4, a0) : u32x4{});
             lds_write16(vslice, off + 16, tok_valid ? __builtin_bit_cast(u32x4, a1) : u32x4{});
+          }
+        }
+        barrier_lds();
+
+        // ---------------- QK^T from the bf16 tile: S^T[32 tokens x 16 heads] in two token blocks.
+        // Step (c, h) multiplies dims 64c + 16*q4 + 8h .. +7 of token 16tb + t16 (slice c/2 of the
+        // tile) with the same dims of Q.
+        f32x4 sacc[2] = {f32x4{}, f32x4{}};
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const char* kslice = smem + C::kOffV + (c >> 1) * C::kVBytes + ((c & 1) * 64 + 16 * q4) * 2;
+#pragma unroll
+          for (int tb = 0; tb < 2; ++tb) {
+            const char* kp = kslice + (16 * tb + t16) * C::kVStride;
+            const bf16x8 a0 = __builtin_bit_cast(bf16x8, lds_read16(kp, 0));
+            const bf16x8 a1 = __builtin_bit_cast(bf16x8, lds_read16(kp, 16));
+            sacc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qreg[c][0], sacc[tb], 0, 0, 0);
+            sacc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qreg[c][1], sacc[tb], 0, 0, 0);
           }
         }
 
@@ -420,7 +451,12 @@ void sparse_decode_kernel(DecodeParams p) {
           }
         }
       }
+#pragma unroll
+      for (int j = 0; j < kDepth; ++j) mk[j] = mk[j + 1];
     }
+    // the copies issued past the segment's end land in unused slots; drain them before the slots
+    // and the index ring are reused
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 
     // ---------------- epilogue for this row segment

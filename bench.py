@@ -32,19 +32,21 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 METRIC = "sparse MLA decode TFLOP/s + KV GB/s, fp8 528B/tok, B=128 H=128 topk=2048"
-DECODE_SRCS = [os.path.join(ROOT, "sparse_mla_decode_get_amd", "csrc", f)
-               for f in ("mla_decode_wide.hip", "mla_decode.hip")]
+CSRC = os.path.join(ROOT, "sparse_mla_decode_get_amd", "csrc")
+# decode kernel source (and the headers it includes) for head counts above 64 and up to 64
+DECODE_SRCS = {True: ["mla_decode_wide.hip", "mla_device.h", "mla_internal.h"],
+               False: ["mla_decode.hip", "mla_device.h", "mla_internal.h"]}
 
 
-def kernel_source_hash() -> str:
-    """Hash of the decode kernel sources (the stored counter traffic is valid only for them)."""
+def kernel_source_hash(wide: bool) -> str:
+    """Hash of the decode kernel's sources (stored counter traffic is valid only for them)."""
     h = hashlib.sha256()
-    for f in DECODE_SRCS:
-        h.update(open(f, "rb").read())
+    for f in DECODE_SRCS[wide]:
+        h.update(open(os.path.join(CSRC, f), "rb").read())
     return h.hexdigest()[:16]
 
 
-def stored_traffic(config: int):
+def stored_traffic(config: int, wide: bool):
     """HBM bytes per launch measured with rocprofv3 --pmc for this decode kernel source, if the
     committed counter summary was taken on the current kernel; otherwise None."""
     path = os.path.join(ROOT, "profiles", f"mla_decode_config{config}_pmc.md")
@@ -53,7 +55,7 @@ def stored_traffic(config: int):
     text = open(path).read()
     m_sha = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
     m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not m_sha or not m_b or m_sha.group(1) != kernel_source_hash():
+    if not m_sha or not m_b or m_sha.group(1) != kernel_source_hash(wide):
         return None
     return float(m_b.group(1))
 
@@ -192,7 +194,7 @@ def main():
         roof = {"bound": "hbm", "achieved": alg_bytes / (per_launch_ms * 1e-3) / 1e9,
                 "peak": HBM_PEAK_GBS, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = stored_traffic(args.config)
+    roof["traffic"] = stored_traffic(args.config, h > 64)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -226,7 +228,7 @@ def main():
         "per_launch_ms": per_launch_ms,
         "wall_s_timed": wall,
         "gen_s": t_gen,
-        "kernel_source_sha256_16": kernel_source_hash(),
+        "kernel_source_sha256_16": kernel_source_hash(h > 64),
         "roofline": roof,
         "cpu_baseline": cpu,
     }

@@ -972,8 +972,14 @@ void sparse_decode_wide_kernel(DecodeParams p) {
           if (i == 0) mfma_qk_first(s_acc, kb[0], qreg[0]);
           else mfma_qk(s_acc, kb[i % kRing], qreg[i]);
           // extra k-step after the last one: the ignored score for ignored tokens of s+1, +0 for
-          // the others (its operands are built two steps earlier)
-          if (i == 31) mfma_qk(s_acc, kflag, qflag);
+          // the others (its operands are built two steps earlier); a sub-tile whose 32 tokens are
+          // all valid needs none
+          if (i == 31 && mk1 != 0xFFFFFFFFu) {
+            // the compiler may build the operands' constant parts right before this step: two
+            // wait states separate those VALU writes from the MFMA's read
+            asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+                         : "+v"(s_acc) : "v"(kflag), "v"(qflag));
+          }
           if (i == 1) {
             sc2 = *reinterpret_cast<const uint16_t*>(draw + (32 * kSubTokens + t) * 16 + c0 / 2);
             rr[0] = lds_read16(draw + ((c0 + 0) * kSubTokens + t) * 16);
@@ -1002,7 +1008,7 @@ void sparse_decode_wide_kernel(DecodeParams p) {
           } else if (i == 8) {
             copy16_to_lds_masked(grec + 512, __builtin_amdgcn_readfirstlane(graw + 32 * 512), scale_lanes_fp8);
           }
-          if (i == 29) {
+          if (i == 29 && mk1 != 0xFFFFFFFFu) {
             // (the B operand's dim 9 in lanes 32..63 also holds the ignored score; A is 0 there)
             uint32_t f0, g0;
             const uint64_t ign = (uint64_t)(uint32_t)~mk1;

@@ -58,8 +58,8 @@ const char* mla_error_string(int code);
  * The metadata partitions the units of all rows over parts: a row owns ceil(topk/64) fp8 units then
  * ceil(extra_topk/64) fp4 units (at least one unit in all); U = R * units_per_row; the part count is
  * P_eff = max(1, min(num_parts, U / min_tiles_per_part)). num_parts == 0 selects the library's
- * default for the current device and h_q (one part per CU for h_q > 64, two per CU for 64-head
- * groups, divided by the number of head groups) and raises min_tiles_per_part to at least 4.
+ * default for the current device and h_q (one part per CU, divided by the number of head groups)
+ * and raises min_tiles_per_part to at least 4.
  * Returns MLA_OK and writes *num_parts_used (host).
  * The pages call for "tile-scheduler metadata computed once before the decode loop" and "split
  * decoding with num_splits" (page "flops/flashmla-decode-fp8-fp4-kv", section "Workarounds"); the

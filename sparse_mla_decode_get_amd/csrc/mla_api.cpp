@@ -35,9 +35,9 @@ int default_parts(int h_q) {
     if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
       cus = v;
   }
-  // workgroups resident per CU: a 128-head group uses about 150 KB of LDS and all registers of
-  // its CU; 64-head groups fit twice (about 75 KB of LDS each)
-  const int per_cu = wide_for(h_q) ? 1 : 2;
+  // one workgroup per CU: a 128-head group uses about 150 KB of LDS and all registers of its CU,
+  // a 64-head group's two halves of four waves about 150 KB of LDS and two waves per SIMD
+  const int per_cu = 1;
   const int parts = cus * per_cu / head_groups(h_q);
   return parts > 0 ? parts : 1;
 }

@@ -9,9 +9,11 @@
 //
 // Work decomposition. The grid is (parts, head groups). A workgroup takes the contiguous range of
 // (row, 64-slot unit) work the tile-scheduler metadata gives its part, for HG query heads
-// (HG = 64 here) with W = HG / 16 = 4 waves, one workgroup per CU. Every wave has the same
-// register footprint: Q of 16 heads (64 VGPRs) and an fp32 output accumulator of 8 MFMA blocks.
-// Each 64-slot unit runs as two sub-tiles of 32 tokens:
+// (HG = 64 here). The workgroup is two halves of W = HG / 16 = 4 waves (eight waves, two per SIMD,
+// one workgroup per CU); half h takes the sub-tiles s = h (mod 2) of the part with its own LDS
+// areas, and the halves' softmax states are merged by log-sum-exp at the end of each row segment.
+// Every wave has the same register footprint: Q of 16 heads (64 VGPRs) and an fp32 output
+// accumulator of 8 MFMA blocks. Each 64-slot unit runs as two sub-tiles of 32 tokens:
 //   1. indices  each wave copies the sub-tile's 32 index entries into its LDS index ring
 //               (global_load_lds_dword), 2 * kDepth sub-tiles ahead of the compute.
 //   2. gather   all lanes copy 16-byte chunks of the selected records (data and scales together,
@@ -33,7 +35,9 @@
 //   6. PV       wave w accumulates O^T[its dim slice x all HG heads] += V^T P^T with
 //               v_mfma_f32_32x32x16_bf16; V^T comes from its own tile slice via ds_read_b64_tr_b16,
 //               P^T from LDS.
-//   7. epilogue one split: out = O / l in bf16 and lse = ln(2) * (m + log2 l); several splits: the
+//   7. merge    half 1 passes its per-head maximum and sum and its unnormalised O to half 0 through
+//               LDS; half 0 rescales both to the larger maximum and adds them.
+//   8. epilogue one split: out = O / l in bf16 and lse = ln(2) * (m + log2 l); several splits: the
 //               normalised fp32 partial and its lse go to the workspace for the merge kernel.
 
 #include "mla_device.h"
@@ -44,6 +48,9 @@ namespace mla {
 // Gather distance in sub-tiles: the records of sub-tile s + kDepth are requested while sub-tile s
 // is computed, and its index entries kDepth sub-tiles before that.
 constexpr int kDepth = 1;
+// Each workgroup runs two independent halves of W waves over the even and odd sub-tiles of its
+// part (two waves per SIMD), merged by log-sum-exp at the end of every row segment.
+constexpr int kHalves = 2;
 
 template <int W>
 struct DecodeCfg {
@@ -74,7 +81,8 @@ struct DecodeCfg {
   static_assert(kDB * kHB == 8, "every wave holds 8 output blocks");
   static_assert(W * kNQ * 2 >= kFp8Chunks, "the copies cover an fp8 record");
   static_assert(kOffIdx % 16 == 0 && kOffDummy % 16 == 0, "aligned LDS areas");
-  static_assert(kLdsBytes + kRawSlots * kRawSlotBytes <= 160 * 1024, "LDS of one workgroup");
+  static_assert(kHalves * (kLdsBytes + kRawSlots * kRawSlotBytes) <= 160 * 1024, "LDS of one workgroup");
+  static_assert(kLdsBytes % 16 == 0 && (kRawSlots * kRawSlotBytes) % 16 == 0, "aligned halves");
   static_assert(kVmcntAfterOldest < 64, "vmcnt counts up to 63");
 };
 
@@ -169,14 +177,25 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 }
 
 template <int W, bool EXTRA>
-__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(64 * W * kHalves) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void sparse_decode_kernel(DecodeParams p) {
   using C = DecodeCfg<W>;
-  __shared__ __attribute__((aligned(16))) char smem[C::kLdsBytes];
-  __shared__ __attribute__((aligned(16))) char rawbuf[C::kRawSlots * C::kRawSlotBytes];   // gathered records
+  constexpr int kRawHalfBytes = C::kRawSlots * C::kRawSlotBytes;
+  // both halves' areas, then both halves' gathered records; at the end of a row segment the whole
+  // array holds the merge's exchange (half 1's O, then every half's m and l)
+  constexpr int kMergeOBytes = W * C::kDB * C::kHB * 16 * 64 * 4;
+  static_assert(kMergeOBytes + kHalves * 2 * C::HG * 4 <= kHalves * (C::kLdsBytes + kRawHalfBytes),
+                "the merge exchange fits in the workgroup's LDS");
+  __shared__ __attribute__((aligned(16))) char lds[kHalves * (C::kLdsBytes + kRawHalfBytes)];
 
   // The wave index is uniform: keep it (and everything derived from it) in scalar registers.
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // Half h (waves hW .. hW+W-1) takes the sub-tiles s = h (mod 2) of the part, with its own LDS
+  // areas; `wave` is the index inside the half.
+  const int wave_all = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int half = wave_all / W;
+  const int wave = wave_all % W;
+  char* const smem = lds + half * C::kLdsBytes;
+  char* const rawbuf = lds + kHalves * C::kLdsBytes + half * kRawHalfBytes;
   const int head_base = blockIdx.y * C::HG;
 
   char* vslice = smem + C::kOffV + wave * C::kVBytes;
@@ -235,13 +254,15 @@ void sparse_decode_kernel(DecodeParams p) {
     float m_run = -__builtin_inff();
     float l_run = 0.0f;
 
-    // ---- asynchronous stages. Sub-tile j's 32 index entries are copied to this wave's index ring
-    // slot j % kIdxSlots, 2 * kDepth sub-tiles ahead of its compute; its records are gathered into
-    // raw slot j % kRawSlots kDepth sub-tiles ahead. Every wave issues exactly kNQ record copies
-    // and one index copy per sub-tile, all with a non-empty EXEC, whatever the sub-tile holds
-    // (ignored tokens, the missing 34th chunk of an fp8 record and an fp4 sub-tile's unused copies
-    // read a zero record; unused copies land in a dummy LDS area), so that one s_waitcnt with a
-    // fixed count waits for exactly the oldest sub-tile.
+    // ---- asynchronous stages, per half. Iteration k of half h handles sub-tile j = 2k + h. Its 32
+    // index entries are copied to this wave's index ring slot k % kIdxSlots, 2 * kDepth iterations
+    // ahead of its compute; its records are gathered into raw slot k % kRawSlots kDepth iterations
+    // ahead. Every wave issues exactly kNQ record copies and one index copy per iteration, all with
+    // a non-empty EXEC, whatever the sub-tile holds (ignored tokens, the missing 34th chunk of an
+    // fp8 record, an fp4 sub-tile's unused copies and sub-tiles past the segment read a zero
+    // record; unused copies land in a dummy LDS area), so that one s_waitcnt with a fixed count
+    // waits for exactly the oldest iteration's copies.
+    const int nk = (nsub + kHalves - 1) / kHalves;     // iterations of each half
     const uint32_t idx_ring = lds_addr(smem + C::kOffIdx + wave * C::kIdxSlots * kSubTokens * 4);
     auto sub_count = [&](int j, int& pos0, bool& fp4) -> int {   // entries of j's index array
       const int unit = t0 + (j >> 1);
@@ -250,7 +271,8 @@ void sparse_decode_kernel(DecodeParams p) {
       pos0 = (unit - p.tiles_k) * kUnitTokens + (j & 1) * kSubTokens;
       return p.extra_topk;
     };
-    auto load_idx = [&](int j) {
+    auto load_idx = [&](int k) {
+      const int j = kHalves * k + half;
       const int32_t* src = p.sched;                  // a valid address when j is past the segment
       if (j < nsub) {
         int pos0;
@@ -259,59 +281,63 @@ void sparse_decode_kernel(DecodeParams p) {
         if (count > 0)
           src = (fp4 ? p.xidx : p.idx) + (int64_t)row * count + min(pos0 + (lane_id() & 31), count - 1);
       }
-      copy4_to_lds_lo32(src, __builtin_amdgcn_readfirstlane(idx_ring + (j % C::kIdxSlots) * kSubTokens * 4));
+      copy4_to_lds_lo32(src, __builtin_amdgcn_readfirstlane(idx_ring + (k % C::kIdxSlots) * kSubTokens * 4));
     };
-    // Gather of sub-tile j (its index entries have landed); returns its validity mask.
-    auto gather = [&](int j) -> uint32_t {
+    // Gather of iteration k's sub-tile (its index entries have landed); returns its validity mask.
+    auto gather = [&](int k) -> uint32_t {
+      const int j = kHalves * k + half;
       const int ln = lane_id();
-      const int t = ln & 31, half = ln >> 5;
+      const int t = ln & 31, hw = ln >> 5;
       int pos0 = 0;
       bool fp4 = false;
       const int count = j < nsub ? sub_count(j, pos0, fp4) : 0;
       const int v = *reinterpret_cast<const int*>(smem + C::kOffIdx +
-                                                  (wave * C::kIdxSlots + j % C::kIdxSlots) * kSubTokens * 4 + 4 * t);
+                                                  (wave * C::kIdxSlots + k % C::kIdxSlots) * kSubTokens * 4 + 4 * t);
       const bool valid = pos0 + t < count && v >= 0;
       const uint32_t bal = (uint32_t)__ballot(valid);
       const int nq = fp4 ? kFp4Chunks / 2 : (kFp8Chunks + 1) / 2;
       const int nch = fp4 ? kFp4Chunks : kFp8Chunks;
       const uint8_t* rec = !valid ? g_zero_record
                                   : fp4 ? p.xc + (int64_t)v * kFp4Rec : p.kc + (int64_t)v * kFp8Rec;
-      const uint32_t raw_lds = lds_addr(rawbuf + (j % C::kRawSlots) * C::kRawSlotBytes);
+      const uint32_t raw_lds = lds_addr(rawbuf + (k % C::kRawSlots) * C::kRawSlotBytes);
 #pragma unroll
       for (int i = 0; i < C::kNQ; ++i) {
         const int qi = wave + W * i;                   // uniform: chunks 2qi (+0) and 2qi+1 (+16)
         const bool used = qi < nq;
-        const uint8_t* src = used && 2 * qi + half < nch ? rec + 32 * qi + 16 * half : g_zero_record;
+        const uint8_t* src = used && 2 * qi + hw < nch ? rec + 32 * qi + 16 * hw : g_zero_record;
         const uint32_t dst = used ? raw_lds + 1024 * qi : lds_addr(smem + C::kOffDummy);
         copy16_to_lds(src, __builtin_amdgcn_readfirstlane(dst));
       }
       return bal;
     };
 
-    // Prologue: index entries of sub-tiles 0 .. kDepth-1 (waited for together with Q), then the
-    // gathers of those sub-tiles, each followed by the index copy kDepth further on, as in the loop.
+    // Prologue: index entries of iterations 0 .. kDepth-1 (waited for together with Q), then the
+    // gathers of those iterations, each followed by the index copy kDepth further on, as in the loop.
 #pragma unroll
-    for (int j = 0; j < kDepth; ++j) load_idx(j);
+    for (int k = 0; k < kDepth; ++k) load_idx(k);
     // vmcnt(0) as a compiler-visible wait, so Q counts as resident for the rest of the segment
     __builtin_amdgcn_s_waitcnt(0x0F70);
-    uint32_t mk[kDepth + 1];                          // validity masks of sub-tiles s .. s+kDepth
+    uint32_t mk[kDepth + 1];                          // validity masks of iterations k .. k+kDepth
 #pragma unroll
-    for (int j = 0; j < kDepth; ++j) {
-      mk[j] = gather(j);
-      load_idx(j + kDepth);
+    for (int k = 0; k < kDepth; ++k) {
+      mk[k] = gather(k);
+      load_idx(k + kDepth);
     }
 
-    for (int s = 0; s < nsub; ++s) {
-      const char* raw = rawbuf + (s % C::kRawSlots) * C::kRawSlotBytes;
+    // Both halves run nk iterations with the same three workgroup barriers each (a half whose
+    // sub-tile is past the segment or fully ignored only skips the work between them).
+    for (int k = 0; k < nk; ++k) {
+      const int s = kHalves * k + half;
+      const char* raw = rawbuf + (k % C::kRawSlots) * C::kRawSlotBytes;
       const uint32_t mask = mk[0];
       int pos0_s;
       bool is_fp4;
       sub_count(s, pos0_s, is_fp4);
-      // The gather of s (and the index entries of s + kDepth) have landed for every wave; every wave
-      // is done with the previous sub-tile's tile, P and raw slot.
+      // The gather of this iteration (and the index entries of iteration k + kDepth) have landed
+      // for every wave; every wave is done with the previous iteration's tile, P and raw slot.
       wait_gather_and_barrier();
-      mk[kDepth] = gather(s + kDepth);
-      load_idx(s + 2 * kDepth);
+      mk[kDepth] = gather(k + kDepth);
+      load_idx(k + 2 * kDepth);
       const int lane = lane_id();
       const int t16 = lane & 15;
       const int q4 = lane >> 4;
@@ -345,8 +371,9 @@ void sparse_decode_kernel(DecodeParams p) {
             lds_write16(vslice, off + 16, tok_valid ? __builtin_bit_cast(u32x4, a1) : u32x4{});
           }
         }
-        barrier_lds();
-
+      }
+      barrier_lds();
+      if (mask != 0) {
         // ---------------- QK^T from the bf16 tile: S^T[32 tokens x 16 heads] in two token blocks.
         // Step (c, h) multiplies dims 64c + 16*q4 + 8h .. +7 of token 16tb + t16 (slice c/2 of the
         // tile) with the same dims of Q.
@@ -459,6 +486,56 @@ void sparse_decode_kernel(DecodeParams p) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 
+    // ---------------- merge of the two halves (log-sum-exp): half 1 hands its running maximum and
+    // sum per head and its unnormalised O to half 0 through LDS; half 0 rescales both to the larger
+    // maximum and adds them. A half that saw no valid token (m = -inf) carries no weight.
+    {
+      float* const obuf = reinterpret_cast<float*>(lds);
+      float* const ml = reinterpret_cast<float*>(lds + kMergeOBytes);   // [half][m, l][head]
+      const int ln = lane_id();
+      const int t16m = ln & 15;
+      if ((ln >> 4) == 0) {
+        ml[(2 * half + 0) * C::HG + 16 * wave + t16m] = m_run;
+        ml[(2 * half + 1) * C::HG + 16 * wave + t16m] = l_run;
+      }
+      if (half == 1) {
+#pragma unroll
+        for (int d = 0; d < C::kDB; ++d)
+#pragma unroll
+          for (int b = 0; b < C::kHB; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              obuf[(((wave * C::kDB + d) * C::kHB + b) * 16 + r) * 64 + ln] = oacc[d][b][r];
+      }
+      __syncthreads();
+      if (half == 0) {
+        const float ninf = -__builtin_inff();
+        auto weights = [&](int hl, float& a0, float& a1, float& m) {
+          const float m0 = ml[0 * C::HG + hl], m1 = ml[2 * C::HG + hl];
+          m = fmaxf(m0, m1);
+          a0 = m0 == ninf ? 0.0f : __builtin_amdgcn_exp2f(m0 - m);
+          a1 = m1 == ninf ? 0.0f : __builtin_amdgcn_exp2f(m1 - m);
+        };
+#pragma unroll
+        for (int b = 0; b < C::kHB; ++b) {
+          float a0, a1, m;
+          weights(32 * b + (ln & 31), a0, a1, m);
+#pragma unroll
+          for (int d = 0; d < C::kDB; ++d)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              oacc[d][b][r] = a0 * oacc[d][b][r] +
+                              a1 * obuf[(((wave * C::kDB + d) * C::kHB + b) * 16 + r) * 64 + ln];
+        }
+        float a0, a1, m;
+        const int hs = 16 * wave + t16m;              // this lane's softmax head
+        weights(hs, a0, a1, m);
+        l_run = a0 * ml[1 * C::HG + hs] + a1 * ml[3 * C::HG + hs];
+        m_run = m;
+      }
+      __syncthreads();
+    }
+
     // ---------------- epilogue for this row segment
     lane = lane_id();
     const int t16e = lane & 15, q4e = lane >> 4, hhe = lane >> 5;
@@ -472,7 +549,7 @@ void sparse_decode_kernel(DecodeParams p) {
     for (int b = 0; b < C::kHB; ++b) {
       const int hl = 32 * b + (lane & 31);
       const int head = head_base + hl;
-      if (head < p.h_q) {
+      if (half == 0 && head < p.h_q) {
         const float l = lfin_s[hl];
         const float inv = l > 0.0f ? 1.0f / l : 0.0f;
 #pragma unroll
@@ -496,7 +573,7 @@ void sparse_decode_kernel(DecodeParams p) {
       }
     }
     const int head_e = head_base + 16 * wave + t16e;
-    if (q4e == 0 && head_e < p.h_q) {
+    if (half == 0 && q4e == 0 && head_e < p.h_q) {
       const float lse = l_run > 0.0f ? (m_run + __log2f(l_run)) * 0.69314718055994530942f
                                      : -__builtin_inff();
       if (final_out)
@@ -515,8 +592,8 @@ int launch_sparse_decode(const DecodeParams& p, int parts, int groups, int waves
   dim3 grid(parts, groups);
   const bool extra = p.extra_topk > 0;
   switch (waves * 2 + (extra ? 1 : 0)) {
-    case 8: hipLaunchKernelGGL((sparse_decode_kernel<4, false>), grid, dim3(256), 0, stream, p); break;
-    case 9: hipLaunchKernelGGL((sparse_decode_kernel<4, true>), grid, dim3(256), 0, stream, p); break;
+    case 8: hipLaunchKernelGGL((sparse_decode_kernel<4, false>), grid, dim3(256 * kHalves), 0, stream, p); break;
+    case 9: hipLaunchKernelGGL((sparse_decode_kernel<4, true>), grid, dim3(256 * kHalves), 0, stream, p); break;
     default: return -1;
   }
   return hipGetLastError() == hipSuccess ? 0 : -1;

@@ -96,7 +96,7 @@ def test_resource_report_parser():
 
 @pytest.mark.parametrize("batch,seq,h_q,topk,extra,min_tiles,expected", [
     (32, 1, 64, 2048, 0, 1, 256),        # 1024 units: at least 4 per part caps the 512 default
-    (64, 1, 64, 2048, 512, 1, 512),      # 2560 units: the 64-head default (2 per CU) stands
+    (64, 1, 64, 2048, 512, 1, 256),      # 2560 units: the default (one part per CU) stands
     (128, 2, 128, 2048, 0, 1, 256),      # headline: one part per CU and row
     (1, 1, 16, 128, 0, 1, 1),            # 2 units: a single part
     (32, 1, 64, 2048, 0, 8, 128),        # a larger caller minimum is kept
@@ -104,11 +104,9 @@ def test_resource_report_parser():
 def test_automatic_part_count_keeps_four_units_per_part(lib, batch, seq, h_q, topk, extra,
                                                        min_tiles, expected):
     # num_parts = 0 selects the device default (256 CUs on MI355X, also the fallback without a
-    # device): CUs x (1 for 128-head groups, 2 for 64-head groups) / head groups, with at least
-    # max(min_tiles_per_part, 4) units per part
+    # device): one part per CU divided by the head groups, with at least max(min_tiles_per_part, 4)
+    # units per part
     p = mla.metadata_parts(batch, seq, h_q, topk, extra, 0, min_tiles)
-    per_cu = 1 if h_q > 64 else 2
     groups = -(-h_q // (128 if h_q > 64 else 64))
-    assert p == part_count(batch * seq, tiles_per_row(topk, extra), 256 * per_cu // groups,
-                           max(min_tiles, 4))
+    assert p == part_count(batch * seq, tiles_per_row(topk, extra), 256 // groups, max(min_tiles, 4))
     assert p == expected

@@ -87,8 +87,9 @@ int mla_get_metadata(int batch, int seq_len_q, int h_q, int topk, int extra_topk
 
 /*
  * Bytes of workspace mla_sparse_decode needs for this schedule: 0 when every part starts on a row
- * boundary (no row is split, the workspace may be NULL); otherwise room for fp32 partial outputs
- * [R + P_eff - 1][h_q][512] followed by fp32 partial lse [R + P_eff - 1][h_q], each 256-byte
+ * boundary (no row is split, the workspace may be NULL); otherwise room for partial outputs
+ * [R + P_eff - 1][h_q][512] (bf16 for h_q <= 64, fp32 above) followed by fp32 partial lse
+ * [R + P_eff - 1][h_q], each 256-byte
  * aligned. Host-only; returns 0 for invalid arguments as well.
  */
 size_t mla_workspace_bytes(int batch, int seq_len_q, int h_q, int topk, int extra_topk,

@@ -121,9 +121,15 @@ int mla_get_metadata(int batch, int seq_len_q, int h_q, int topk, int extra_topk
   return MLA_OK;
 }
 
+// Bytes per partial output value: the 64-head kernel writes bf16 partials (the merge takes them back
+// to fp32), the 128-head kernel fp32 ones (its registers leave no room for the conversion).
+static size_t partial_elem_bytes(int h_q) { return wide_for(h_q) ? sizeof(float) : sizeof(uint16_t); }
+
 static size_t split_workspace_bytes(int batch, int seq_len_q, int h_q, int num_parts_used) {
   const size_t slots = (size_t)batch * seq_len_q + (size_t)num_parts_used - 1;
-  return align256(slots * h_q * MLA_HEAD_DIM * sizeof(float)) + align256(slots * h_q * sizeof(float));
+  // partial outputs, then fp32 partial lse
+  return align256(slots * h_q * MLA_HEAD_DIM * partial_elem_bytes(h_q)) +
+         align256(slots * h_q * sizeof(float));
 }
 
 size_t mla_workspace_bytes(int batch, int seq_len_q, int h_q, int topk, int extra_topk,
@@ -155,15 +161,15 @@ int mla_sparse_decode(const void* q, const uint8_t* k_cache, int64_t k_tokens,
   int tiles_k = 0;
   const int tiles = tiles_per_row(topk, extra_topk, &tiles_k);
   const bool split = any_split(rows, tiles, num_parts_used);
-  float* part_o = nullptr;
+  void* part_o = nullptr;
   float* part_lse = nullptr;
   if (split) {
     const size_t need = split_workspace_bytes(batch, seq_len_q, h_q, num_parts_used);
     if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return MLA_ERR_WORKSPACE;
     const size_t slots = (size_t)rows + (size_t)num_parts_used - 1;
-    part_o = static_cast<float*>(workspace);
+    part_o = workspace;
     part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                        align256(slots * h_q * MLA_HEAD_DIM * sizeof(float)));
+                                        align256(slots * h_q * MLA_HEAD_DIM * partial_elem_bytes(h_q)));
   }
   mla::DecodeParams p;
   p.q = static_cast<const uint16_t*>(q);
@@ -188,8 +194,14 @@ int mla_sparse_decode(const void* q, const uint8_t* k_cache, int64_t k_tokens,
   const int launched = wide_for(h_q) ? mla::launch_sparse_decode_wide(p, num_parts_used, head_groups(h_q), s)
                                      : mla::launch_sparse_decode(p, num_parts_used, head_groups(h_q), 4, s);
   if (launched != 0) return MLA_ERR_HIP;
-  if (split && mla::launch_combine(part_o, part_lse, split_ptr, rows, h_q, p.out, lse, true, s) != 0)
-    return MLA_ERR_HIP;
+  if (split) {
+    const int merged = wide_for(h_q)
+        ? mla::launch_combine(static_cast<const float*>(part_o), part_lse, split_ptr, rows, h_q, p.out,
+                              lse, true, s)
+        : mla::launch_combine_bf16(static_cast<const uint16_t*>(part_o), part_lse, split_ptr, rows,
+                                   h_q, p.out, lse, s);
+    if (merged != 0) return MLA_ERR_HIP;
+  }
   return MLA_OK;
 }
 

@@ -10,8 +10,22 @@ namespace mla {
 
 constexpr int kCombineThreads = 128;   // 4 dims per thread
 
+// Four dims of one partial row as fp32: from fp32 partials (mla_combine's input) or from the bf16
+// partials the decode kernels write to their workspace.
+__device__ __forceinline__ f32x4 load4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+__device__ __forceinline__ f32x4 load4(const uint16_t* p) {
+  const u32x2 w = *reinterpret_cast<const u32x2*>(p);
+  f32x4 r;
+  r[0] = __builtin_bit_cast(float, w[0] << 16);
+  r[1] = __builtin_bit_cast(float, w[0] & 0xFFFF0000u);
+  r[2] = __builtin_bit_cast(float, w[1] << 16);
+  r[3] = __builtin_bit_cast(float, w[1] & 0xFFFF0000u);
+  return r;
+}
+
+template <typename PT>
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
-    const float* __restrict__ partial, const float* __restrict__ partial_lse,
+    const PT* __restrict__ partial, const float* __restrict__ partial_lse,
     const int32_t* __restrict__ split_ptr, int h_q, uint16_t* __restrict__ out,
     float* __restrict__ lse, int skip_single) {
   const int row = blockIdx.x;
@@ -33,7 +47,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
     for (int u = 0; u < kBatch; ++u) m = fmaxf(m, li[u]);
   }
   const int dim = 4 * threadIdx.x;
-  const float* o_col = partial + ((int64_t)a * h_q + head) * kHeadDim + dim;
+  const PT* o_col = partial + ((int64_t)a * h_q + head) * kHeadDim + dim;
   f32x4 acc = f32x4{};
   float wsum = 0.0f;
   if (m != ninf) {
@@ -44,8 +58,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
       for (int u = 0; u < kBatch; ++u) {
         const bool in = i0 + u < n;
         li[u] = in ? lse_col[(int64_t)(i0 + u) * h_q] : ninf;
-        o[u] = in ? *reinterpret_cast<const f32x4*>(o_col + (int64_t)(i0 + u) * h_q * kHeadDim)
-                  : f32x4{};
+        o[u] = in ? load4(o_col + (int64_t)(i0 + u) * h_q * kHeadDim) : f32x4{};
       }
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) {
@@ -68,8 +81,15 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
 int launch_combine(const float* partial, const float* partial_lse, const int32_t* split_ptr,
                    int rows, int h_q, uint16_t* out, float* lse, bool skip_single,
                    hipStream_t stream) {
-  hipLaunchKernelGGL(combine_kernel, dim3(rows, h_q), dim3(kCombineThreads), 0, stream, partial,
-                     partial_lse, split_ptr, h_q, out, lse, skip_single ? 1 : 0);
+  hipLaunchKernelGGL(combine_kernel<float>, dim3(rows, h_q), dim3(kCombineThreads), 0, stream,
+                     partial, partial_lse, split_ptr, h_q, out, lse, skip_single ? 1 : 0);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int launch_combine_bf16(const uint16_t* partial, const float* partial_lse, const int32_t* split_ptr,
+                        int rows, int h_q, uint16_t* out, float* lse, hipStream_t stream) {
+  hipLaunchKernelGGL(combine_kernel<uint16_t>, dim3(rows, h_q), dim3(kCombineThreads), 0, stream,
+                     partial, partial_lse, split_ptr, h_q, out, lse, 1);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -38,7 +38,8 @@
 //   7. merge    half 1 passes its per-head maximum and sum and its unnormalised O to half 0 through
 //               LDS; half 0 rescales both to the larger maximum and adds them.
 //   8. epilogue one split: out = O / l in bf16 and lse = ln(2) * (m + log2 l); several splits: the
-//               normalised fp32 partial and its lse go to the workspace for the merge kernel.
+//               normalised partial (bf16) and its lse (fp32) go to the workspace for the merge
+//               kernel.
 
 #include "mla_device.h"
 #include "mla_internal.h"
@@ -557,17 +558,14 @@ void sparse_decode_kernel(DecodeParams p) {
 #pragma unroll
           for (int jb = 0; jb < 4; ++jb) {
             const int dim = wave * C::kSlice + 32 * d + 8 * jb + 4 * hhe;
-            if (final_out) {
-              bf16x4 o;
+            // the final row, or this split's normalised partial (bf16 as well: the merge takes it
+            // back to fp32 and weights it)
+            bf16x4 o;
 #pragma unroll
-              for (int i = 0; i < 4; ++i) o[i] = (__bf16)(oacc[d][b][4 * jb + i] * inv);
-              *reinterpret_cast<bf16x4*>(p.out + ((int64_t)row * p.h_q + head) * kHeadDim + dim) = o;
-            } else {
-              f32x4 o;
-#pragma unroll
-              for (int i = 0; i < 4; ++i) o[i] = oacc[d][b][4 * jb + i] * inv;
-              *reinterpret_cast<f32x4*>(p.part_o + ((int64_t)slot * p.h_q + head) * kHeadDim + dim) = o;
-            }
+            for (int i = 0; i < 4; ++i) o[i] = (__bf16)(oacc[d][b][4 * jb + i] * inv);
+            uint16_t* const dst = final_out ? p.out + ((int64_t)row * p.h_q + head) * kHeadDim
+                                            : static_cast<uint16_t*>(p.part_o) + ((int64_t)slot * p.h_q + head) * kHeadDim;
+            *reinterpret_cast<bf16x4*>(dst + dim) = o;
           }
         }
       }

@@ -1248,7 +1248,7 @@ void sparse_decode_wide_kernel(DecodeParams p) {
             f32x4 o;
 #pragma unroll
             for (int i = 0; i < 4; ++i) o[i] = oacc[d][4 * jb + i] * inv;
-            *reinterpret_cast<f32x4*>(p.part_o + ((int64_t)slot * p.h_q + head) * kHeadDim + dim) = o;
+            *reinterpret_cast<f32x4*>(static_cast<float*>(p.part_o) + ((int64_t)slot * p.h_q + head) * kHeadDim + dim) = o;
           }
           __builtin_amdgcn_sched_barrier(0);
         }

@@ -18,7 +18,8 @@ struct DecodeParams {
   float scale_log2;          // softmax_scale * log2(e)
   const int32_t* sched;      // [parts][8]
   const int32_t* split_ptr;  // [rows + 1]
-  float* part_o;             // workspace partial outputs [slots][h_q][512]
+  void* part_o;              // workspace partial outputs [slots][h_q][512]: fp32 from the 128-head
+                             // kernel, bf16 from the 64-head kernel
   float* part_lse;           // workspace partial lse [slots][h_q]
   uint16_t* out;             // bf16 [rows][h_q][512]
   float* lse;                // [rows][h_q]
@@ -29,9 +30,14 @@ int launch_sparse_decode(const DecodeParams& p, int parts, int groups, int nw, h
 int launch_sparse_decode_wide(const DecodeParams& p, int parts, int groups, hipStream_t stream);
 int launch_metadata(int rows, int tiles, int parts, int32_t* sched, int32_t* split_ptr,
                     hipStream_t stream);
+// Merge of fp32 partials (mla_combine, and the 128-head decode's workspace) or of the 64-head
+// decode's bf16 partials; after a decode, rows with a single split (written directly by the decode
+// kernel) are skipped.
 int launch_combine(const float* partial, const float* partial_lse, const int32_t* split_ptr,
                    int rows, int h_q, uint16_t* out, float* lse, bool skip_single,
                    hipStream_t stream);
+int launch_combine_bf16(const uint16_t* partial, const float* partial_lse, const int32_t* split_ptr,
+                        int rows, int h_q, uint16_t* out, float* lse, hipStream_t stream);
 int launch_dequant(const uint8_t* cache, int record_bytes, const int32_t* idx, int n,
                    uint16_t* out, hipStream_t stream);
 int launch_validate(const int32_t* idx, int64_t n, int64_t num_tokens, int32_t* bad,

@@ -54,7 +54,7 @@ def test_part_count_and_workspace_match_oracle(lib, batch, seq, topk, extra, par
         assert (ws > 0) == split
         if split:
             slots = batch * seq + p - 1
-            assert ws >= slots * 64 * 512 * 4 + slots * 64 * 4
+            assert ws >= slots * 64 * 512 * 2 + slots * 64 * 4      # bf16 partials, fp32 lse
 
 
 def test_headline_schedule_needs_no_workspace(lib):

@@ -261,3 +261,63 @@ def test_full_size_workloads_sampled_rows(cfg, rows):
     assert torch.isfinite(out.float()).all()
     valid_rows = (torch.from_numpy(w["indices"]).reshape(nrows, -1) >= 0).any(dim=1)
     assert torch.isfinite(lse.reshape(nrows, -1)[valid_rows.cuda()]).all()
+
+
+@pytest.mark.parametrize("h_q,extra", [(128, 0), (64, 0), (64, 40)])
+def test_duplicate_entries_count_with_multiplicity(h_q, extra):
+    """Every selected token listed twice (the row's second half repeats its first half), and one row
+    that lists a single token 300 times: the softmax runs over the list as given, so the output is
+    that of the distinct tokens and lse grows by ln 2 (resp. equals s + ln 300)."""
+    spec = Spec("dups", 2, 1, h_q, 300, 2048, extra_topk=extra,
+                extra_tokens_per_seq=1024 if extra else 0)
+    w = make_workload(spec, seed=41)
+    base_out, base_lse = _oracle(w)
+    idx = w["indices"]
+    idx[:, :, 150:] = idx[:, :, :150]                    # every entry twice
+    idx[1, 0, :] = idx[1, 0, 7]                          # row 1: one token, 300 times
+    if extra:
+        w["extra_indices"][:, :, 20:] = w["extra_indices"][:, :, :20]
+    ref_out, ref_lse = _oracle(w)
+    out, lse, _ = _decode(w)
+    check_rows(out, lse, ref_out, ref_lse, f"dups/h{h_q}")
+    assert np.isfinite(ref_lse).all()
+    # the oracle's own reading of duplicates, for the doubled row 0
+    if not extra:
+        half = dict(w)
+        half["indices"] = idx[:, :, :150].copy()
+        h_out, h_lse = _oracle(half)
+        assert np.allclose(ref_lse[0], h_lse[0] + math.log(2.0), atol=1e-9)
+
+
+def test_decode_replays_from_a_captured_graph():
+    """The decode step captured in a HIP graph (through torch.cuda.CUDAGraph): every replay, with
+    eager work on the same stream between replays, matches the eager result bit for bit."""
+    spec = Spec("graph", 4, 2, 128, 700, 4096, neg="tail10")
+    w = make_workload(spec, seed=51)
+    d = to_dev(w)
+    md = mla.get_metadata(4, 2, 128, 700, 0, num_parts=13)      # rows split: decode + merge
+    assert md.workspace is not None
+    out = torch.empty((4, 2, 128, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((4, 2, 128), dtype=torch.float32, device="cuda")
+    mla.sparse_decode(d["q"], d["k_cache"], d["indices"], w["softmax_scale"], md, out=out, lse=lse)
+    torch.cuda.synchronize()
+    eager_out, eager_lse = out.clone(), lse.clone()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            mla.sparse_decode(d["q"], d["k_cache"], d["indices"], w["softmax_scale"], md,
+                              out=out, lse=lse)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for k in range(3):
+        out.fill_(k + 1.0)                                  # eager work between the replays
+        lse.fill_(-1.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager_out), f"replay {k}: output differs from the eager decode"
+        assert torch.equal(lse, eager_lse), f"replay {k}: lse differs from the eager decode"
+    ref_out, ref_lse = _oracle(w)
+    check_rows(out, lse, ref_out, ref_lse, "graph")

@@ -159,20 +159,19 @@ def main():
         step(k)
     torch.cuda.synchronize()
 
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    # HIP events on the launch stream bracket the timed region only: an event recorded between
+    # two launches costs the GPU several microseconds, so per-step events would time themselves
+    # along with short steps
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     e0.record(stream)
     for k in range(args.steps):
-        starts[k].record(stream)
         step(k)
-        ends[k].record(stream)
     e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     total_ms = e0.elapsed_time(e1)
-    per_launch_ms = float(np.mean([a.elapsed_time(z) for a, z in zip(starts, ends)]))
+    per_launch_ms = total_ms / args.steps      # one decode call (decode kernel, plus the merge)
     ms_per_step = total_ms / args.steps
 
     # algorithmic work per step (valid tokens only), averaged over the index sets the steps used

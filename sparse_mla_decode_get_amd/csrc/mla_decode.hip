@@ -23,8 +23,9 @@
 //               A fixed number of copies per wave and sub-tile lets one s_waitcnt wait for
 //               exactly the oldest sub-tile while the newer ones stay in flight.
 //   3. dequant  wave w converts its 512 / W dims of the 32 tokens to bf16 (the record's own scale,
-//               in registers) into its slice of the LDS tile, zeroing ignored tokens; the W slices
-//               form the sub-tile's bf16 tile, written once and read by every wave.
+//               in registers) into its slice of the LDS tile (an ignored token's zero record
+//               decodes to zeros); the W slices form the sub-tile's bf16 tile, written once and
+//               read by every wave.
 //   4. QK^T     wave w owns heads 16w..16w+15: v_mfma_f32_16x16x32_bf16 of tile rows (conflict-free
 //               ds_read_b128) against its register-resident Q, S^T[16 tokens x 16 heads] over all
 //               512 dims.
@@ -344,12 +345,12 @@ void sparse_decode_kernel(DecodeParams p) {
       const int q4 = lane >> 4;
       const int hh = lane >> 5;
       if (mask != 0) {
-        // ---------------- this wave's dim slice of the sub-tile's 32 tokens, raw -> bf16 tile slice
-        // (zero for ignored tokens); the four slices make up the tile that QK^T and PV read.
+        // ---------------- this wave's dim slice of the sub-tile's 32 tokens, raw -> bf16 tile slice;
+        // the four slices make up the tile that QK^T and PV read. An ignored token's record is the
+        // zero record (all bytes 0, scale byte 0), which decodes to exact +0.
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb) {
           const int t = 16 * tb + t16;
-          const bool tok_valid = (mask >> t) & 1u;
 #pragma unroll
           for (int cs = 0; cs < C::kSlice / 64; ++cs) {
             const int c = wave * (C::kSlice / 64) + cs;                       // uniform
@@ -368,8 +369,8 @@ void sparse_decode_kernel(DecodeParams p) {
               dequant_fp4_16(r[0], r[1], e4m3_to_f32(sb), a0, a1);
             }
             const int off = t * C::kVStride + (64 * cs + 16 * q4) * 2;
-            lds_write16(vslice, off, tok_valid ? __builtin_bit_cast(u32x4, a0) : u32x4{});
-            lds_write16(vslice, off + 16, tok_valid ? __builtin_bit_cast(u32x4, a1) : u32x4{});
+            lds_write16(vslice, off, __builtin_bit_cast(u32x4, a0));
+            lds_write16(vslice, off + 16, __builtin_bit_cast(u32x4, a1));
           }
         }
       }
@@ -395,16 +396,26 @@ void sparse_decode_kernel(DecodeParams p) {
         // ---------------- online softmax for head 16*wave + t16; sacc[tb][i] is token 16tb+4q4+i
         float x[8];
         float mx = -__builtin_inff();
-        const uint32_t mq = mask >> (4 * q4);
+        if (mask == 0xFFFFFFFFu) {                   // all 32 tokens valid: no masking
 #pragma unroll
-        for (int tb = 0; tb < 2; ++tb)
+          for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float v = ((mq >> (16 * tb + i)) & 1u) ? sacc[tb][i] * p.scale_log2
-                                                          : -__builtin_inff();
-            x[4 * tb + i] = v;
-            mx = fmaxf(mx, v);
-          }
+            for (int i = 0; i < 4; ++i) {
+              x[4 * tb + i] = sacc[tb][i] * p.scale_log2;
+              mx = fmaxf(mx, x[4 * tb + i]);
+            }
+        } else {
+          const uint32_t mq = mask >> (4 * q4);
+#pragma unroll
+          for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float v = ((mq >> (16 * tb + i)) & 1u) ? sacc[tb][i] * p.scale_log2
+                                                            : -__builtin_inff();
+              x[4 * tb + i] = v;
+              mx = fmaxf(mx, v);
+            }
+        }
         mx = fmaxf(mx, xor16(mx, lane));
         mx = max_xor32(mx);
         const float m_new = fmaxf(m_run, mx);

@@ -110,3 +110,28 @@ def test_automatic_part_count_keeps_four_units_per_part(lib, batch, seq, h_q, to
     groups = -(-h_q // (128 if h_q > 64 else 64))
     assert p == part_count(batch * seq, tiles_per_row(topk, extra), 256 // groups, max(min_tiles, 4))
     assert p == expected
+
+
+def test_host_checks_reject_bad_workspace_scale_and_alignment(lib):
+    """These checks run on the host before anything is enqueued, so dummy (never dereferenced)
+    device addresses suffice: a split schedule without enough workspace, a non-finite softmax
+    scale and a misaligned q are refused with their documented codes."""
+    L = lib
+    batch, seq, h_q, topk, parts = 2, 1, 64, 256, 5          # 8 units over 5 parts: rows split
+    p = mla.metadata_parts(batch, seq, h_q, topk, 0, parts, 1)
+    need = mla.workspace_bytes(batch, seq, h_q, topk, 0, p)
+    assert need > 0
+    a = 1 << 20                                              # dummy 256-byte aligned addresses
+    q, kc, idx, sched, sp, out, lse, ws = (a * i for i in range(1, 9))
+    tokens = 4096
+
+    def decode(scale=0.04, qp=q, ws_ptr=ws, ws_bytes=need):
+        return L.mla_sparse_decode(qp, kc, tokens, idx, topk, None, 0, None, 0, batch, seq, h_q, scale,
+                                   sched, sp, p, ws_ptr, ws_bytes, out, lse, None)
+
+    assert decode(ws_ptr=None) == -3                         # MLA_ERR_WORKSPACE: none given
+    assert decode(ws_bytes=need - 1) == -3                   # too small
+    assert decode(ws_ptr=ws + 16) == -3                      # not 256-byte aligned
+    assert decode(scale=float("inf")) == -1                  # MLA_ERR_INVALID_ARG
+    assert decode(scale=float("nan")) == -1
+    assert decode(qp=q + 2) == -1                            # q not 16-byte aligned

@@ -47,8 +47,8 @@
 
 namespace mla {
 
-// Gather distance in sub-tiles: the records of sub-tile s + kDepth are requested while sub-tile s
-// is computed, and its index entries kDepth sub-tiles before that.
+// Gather distance in iterations of a half: the records of iteration k + kDepth are requested while
+// iteration k is computed, and its index entries kDepth iterations before that.
 constexpr int kDepth = 1;
 // Each workgroup runs two independent halves of W waves over the even and odd sub-tiles of its
 // part (two waves per SIMD), merged by log-sum-exp at the end of every row segment.
@@ -221,8 +221,6 @@ void sparse_decode_kernel(DecodeParams p) {
     // Lane-derived indices are recomputed from an opaque copy of the lane id in each row segment
     // (and again in each sub-tile below) rather than kept live across the whole kernel.
     int lane = lane_id();
-    const int tok = lane & 31;      // token of this lane in the gather
-    const int hh = lane >> 5;       // which chunk of a chunk pair this lane gathers
     const int t16 = lane & 15;      // QK^T: token (A operand) / head (B operand, C column)
     const int q4 = lane >> 4;       // QK^T: 16-dim group inside a 64-dim step
     // QK^T role: lane (t16, q4) holds Q of head my_head for dims 64c + 16*q4 .. +15.
@@ -460,7 +458,8 @@ void sparse_decode_kernel(DecodeParams p) {
         }
         const int g = lane >> 4, j = lane & 15;
         typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
-        // V^T operand for (ks, d): two transposed reads of the private slice, lane (dim, 8 tokens)
+        // V^T operand for (ks, d): two transposed reads of the wave's own tile slice, lane (dim,
+        // 8 tokens)
         auto load_v = [&](int ks, int d) -> bf16x8 {
           const int row0 = 16 * ks + 8 * (g >> 1) + (j >> 2);
           const int col = 32 * d + 16 * (g & 1) + 4 * (j & 3);

@@ -54,9 +54,14 @@ constexpr int kGroupHeads = 32 * kWaves;
 // chunk c (dims 8c .. 8c+7) is stored at chunk position c ^ tile_xor(r), which only permutes the
 // chunks within aligned groups of four. The padding moves each row by four 4-bank groups and the
 // XOR picks among the four of a group, so every access pattern of the kernel is free of LDS bank
-// conflicts: 16 rows at one chunk (K row reads, dequant writes) hit 16 different 4-bank groups, and
-// so do 4 rows x 4 consecutive chunks (the transposed V reads). Since the XOR leaves the chunk
-// index above bit 1 alone, operand addresses differ from a few per-lane bases by immediates.
+// conflicts:
+//   - reads are served 256 bytes at a time: 16 rows at one chunk (K row reads) hit 16 different
+//     4-bank groups, and so do 4 rows x 4 consecutive chunks (the transposed V reads);
+//   - 16-byte writes are served 8 lanes (128 bytes, 32 banks) at a time: 8 consecutive rows at one
+//     chunk (the dequant writes) hit 8 different 4-bank groups of 32 banks, which needs different
+//     XOR values among the even rows and among the odd rows of each group of 8.
+// Since the XOR leaves the chunk index above bit 1 alone, operand addresses differ from a few
+// per-lane bases by immediates.
 constexpr int kTileStride = 1088;
 constexpr int kTileBytes = kSubTokens * kTileStride;    // 34816
 constexpr int kRawBytes = kFp8Chunks * kSubTokens * 16; // 16896, chunk-major [chunk][token][16 B]
@@ -196,7 +201,9 @@ __device__ __forceinline__ void wait_and_barrier(int n) {
   }
 }
 
-__device__ __forceinline__ int tile_xor(int r) { return (r >> 2) & 3; }
+// The XOR pattern of token row r: bit 1 = bit 1 ^ bit 3 of r, bit 0 = bit 2 of r (the same for r and
+// r + 16).
+__device__ __forceinline__ int tile_xor(int r) { return (((r >> 1) ^ (r >> 3)) & 1) * 2 + ((r >> 2) & 1); }
 
 __device__ __forceinline__ u32x4 lds_read16(const char* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void lds_write16(char* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }

@@ -35,40 +35,41 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
   if (skip_single && n == 1) return;      // written directly by the decode kernel
   const float ninf = -__builtin_inff();
   const float* lse_col = partial_lse + (int64_t)a * h_q + head;
-  // Splits are taken kBatch at a time with all their loads issued before any is used, so a row
-  // with many splits costs a few memory round trips rather than one per split.
-  constexpr int kBatch = 8;
-  float m = ninf;
-  for (int i0 = 0; i0 < n; i0 += kBatch) {
-    float li[kBatch];
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) li[u] = i0 + u < n ? lse_col[(int64_t)(i0 + u) * h_q] : ninf;
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) m = fmaxf(m, li[u]);
-  }
   const int dim = 4 * threadIdx.x;
   const PT* o_col = partial + ((int64_t)a * h_q + head) * kHeadDim + dim;
+  // One pass over the splits, kBatch at a time, with every lse and partial load of a batch issued
+  // before any is used (one memory round trip per batch, none waiting on an earlier maximum). The
+  // sums are kept relative to the running maximum m and rescaled when a batch raises it:
+  // wsum = sum_i exp(lse_i - m), acc = sum_i exp(lse_i - m) o_i.
+  constexpr int kBatch = 8;
+  float m = ninf;
   f32x4 acc = f32x4{};
   float wsum = 0.0f;
-  if (m != ninf) {
-    for (int i0 = 0; i0 < n; i0 += kBatch) {
-      float li[kBatch];
-      f32x4 o[kBatch];
+  for (int i0 = 0; i0 < n; i0 += kBatch) {
+    float li[kBatch];
+    f32x4 o[kBatch];
 #pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        const bool in = i0 + u < n;
-        li[u] = in ? lse_col[(int64_t)(i0 + u) * h_q] : ninf;
-        o[u] = in ? load4(o_col + (int64_t)(i0 + u) * h_q * kHeadDim) : f32x4{};
-      }
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        // an empty split (lse -inf) carries no weight, whatever its partial holds
-        if (li[u] == ninf) continue;
-        const float w = __expf(li[u] - m);
-        wsum += w;
-        acc += w * o[u];
-      }
+    for (int u = 0; u < kBatch; ++u) {
+      const bool in = i0 + u < n;
+      li[u] = in ? lse_col[(int64_t)(i0 + u) * h_q] : ninf;
+      o[u] = in ? load4(o_col + (int64_t)(i0 + u) * h_q * kHeadDim) : f32x4{};
     }
+    float mb = m;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) mb = fmaxf(mb, li[u]);
+    if (mb == ninf) continue;                // no live split so far
+    const float sc = __expf(m - mb);         // 0 while m = -inf, when acc and wsum are still 0
+    acc *= sc;
+    wsum *= sc;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      // an empty split (lse -inf) carries no weight, whatever its partial holds
+      if (li[u] == ninf) continue;
+      const float w = __expf(li[u] - mb);
+      wsum += w;
+      acc += w * o[u];
+    }
+    m = mb;
   }
   const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
   bf16x4 r;

@@ -226,6 +226,25 @@ def test_combine_matches_oracle_merge():
     check_rows(out, lse, ref_out, ref_lse, "combine")
 
 
+def test_combine_many_splits_across_batches():
+    # rows of 1, 9, 20 and 17 splits: the merge takes splits eight at a time, so the running maximum
+    # rises between batches; row 3's first batch is all empty, and its lse spread is wide
+    rng = np.random.default_rng(11)
+    counts = [1, 9, 20, 17]
+    split_ptr = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    s, h = int(split_ptr[-1]), 8
+    po = rng.standard_normal((s, h, 512)).astype(np.float32)
+    pl = rng.uniform(-30.0, 30.0, (s, h)).astype(np.float32)
+    pl[split_ptr[2] + 3] = -np.inf                   # a dead split inside a batch
+    pl[split_ptr[3]:split_ptr[3] + 8] = -np.inf      # row 3: its first batch has no live split
+    pl[split_ptr[3] + 12, :4] = 80.0                 # a later batch raises the maximum a lot
+    ref_out, ref_lse = oracle_combine(po.astype(np.float64), pl.astype(np.float64), split_ptr)
+    out, lse = mla.combine(torch.from_numpy(po).cuda(), torch.from_numpy(pl).cuda(),
+                           torch.from_numpy(split_ptr).cuda())
+    torch.cuda.synchronize()
+    check_rows(out, lse, ref_out, ref_lse, "combine, many splits")
+
+
 def test_combine_all_empty_splits():
     po = torch.zeros((3, 4, 512), device="cuda")
     pl = torch.full((3, 4), -math.inf, device="cuda")

@@ -189,6 +189,10 @@ void sparse_decode_kernel(DecodeParams p) {
   static_assert(kMergeOBytes + kHalves * 2 * C::HG * 4 <= kHalves * (C::kLdsBytes + kRawHalfBytes),
                 "the merge exchange fits in the workgroup's LDS");
   __shared__ __attribute__((aligned(16))) char lds[kHalves * (C::kLdsBytes + kRawHalfBytes)];
+  // epilogue staging of the bf16 output rows (16 bytes of padding per 1 KB row)
+  constexpr int kStageRow = 2 * kHeadDim + 16;
+  static_assert(C::kLdsBytes + C::HG * kStageRow <= kHalves * (C::kLdsBytes + kRawHalfBytes),
+                "the output staging fits in the workgroup's LDS past half 0's area");
 
   // The wave index is uniform: keep it (and everything derived from it) in scalar registers.
   // Half h (waves hW .. hW+W-1) takes the sub-tiles s = h (mod 2) of the part, with its own LDS
@@ -203,7 +207,6 @@ void sparse_decode_kernel(DecodeParams p) {
   char* vslice = smem + C::kOffV + wave * C::kVBytes;
   char* pbuf = smem + C::kOffP;
   float* alpha_s = reinterpret_cast<float*>(smem + C::kOffAlpha);
-  float* mfin_s = reinterpret_cast<float*>(smem + C::kOffMFin);
   float* lfin_s = reinterpret_cast<float*>(smem + C::kOffLFin);
   int* flag_s = reinterpret_cast<int*>(smem + C::kOffFlag);
 
@@ -228,9 +231,6 @@ void sparse_decode_kernel(DecodeParams p) {
 
     const int t1 = row < end_row ? p.tiles : end_tile;
     const int nsub = 2 * (t1 - t0);
-    const int split_base = p.split_ptr[row];
-    const int nsplit = p.split_ptr[row + 1] - split_base;
-    const int slot = first_seg ? slot_first : split_base;
 
     // Q (B operand): heads past h_q load a copy of the last head; their results are never stored.
     // Q (B operand): heads past h_q load a copy of the last head; their results are never stored.
@@ -323,6 +323,11 @@ void sparse_decode_kernel(DecodeParams p) {
       mk[k] = gather(k);
       load_idx(k + kDepth);
     }
+    // The split bookkeeping is needed only by the epilogue. It is read after the segment's first
+    // copies are issued, so its memory round trip overlaps theirs instead of delaying the Q load.
+    const int split_base = p.split_ptr[row];
+    const int nsplit = p.split_ptr[row + 1] - split_base;
+    const int slot = first_seg ? slot_first : split_base;
 
     // Both halves run nk iterations with the same three workgroup barriers each (a half whose
     // sub-tile is past the segment or fully ignored only skips the work between them).
@@ -547,20 +552,18 @@ void sparse_decode_kernel(DecodeParams p) {
       __syncthreads();
     }
 
-    // ---------------- epilogue for this row segment
+    // ---------------- epilogue for this row segment. Half 0 normalises O and stages it in bf16 in
+    // LDS (head rows kStageRow bytes apart, past half 0's area); then every wave stores whole 1 KB
+    // head rows, 16 bytes per lane, instead of 16 bytes into each of 32 rows per store instruction.
     lane = lane_id();
     const int t16e = lane & 15, q4e = lane >> 4, hhe = lane >> 5;
-    if (q4e == 0) {
-      mfin_s[16 * wave + t16e] = m_run;
-      lfin_s[16 * wave + t16e] = l_run;
-    }
+    if (half == 0 && q4e == 0) lfin_s[16 * wave + t16e] = l_run;
     __syncthreads();
-    const bool final_out = nsplit == 1;
+    char* const stage = lds + C::kLdsBytes;
+    if (half == 0) {
 #pragma unroll
-    for (int b = 0; b < C::kHB; ++b) {
-      const int hl = 32 * b + (lane & 31);
-      const int head = head_base + hl;
-      if (half == 0 && head < p.h_q) {
+      for (int b = 0; b < C::kHB; ++b) {
+        const int hl = 32 * b + (lane & 31);
         const float l = lfin_s[hl];
         const float inv = l > 0.0f ? 1.0f / l : 0.0f;
 #pragma unroll
@@ -568,16 +571,25 @@ void sparse_decode_kernel(DecodeParams p) {
 #pragma unroll
           for (int jb = 0; jb < 4; ++jb) {
             const int dim = wave * C::kSlice + 32 * d + 8 * jb + 4 * hhe;
-            // the final row, or this split's normalised partial (bf16 as well: the merge takes it
-            // back to fp32 and weights it)
             bf16x4 o;
 #pragma unroll
             for (int i = 0; i < 4; ++i) o[i] = (__bf16)(oacc[d][b][4 * jb + i] * inv);
-            uint16_t* const dst = final_out ? p.out + ((int64_t)row * p.h_q + head) * kHeadDim
-                                            : static_cast<uint16_t*>(p.part_o) + ((int64_t)slot * p.h_q + head) * kHeadDim;
-            *reinterpret_cast<bf16x4*>(dst + dim) = o;
+            *reinterpret_cast<bf16x4*>(stage + hl * kStageRow + 2 * dim) = o;
           }
         }
+      }
+    }
+    __syncthreads();
+    // the final row, or this split's normalised partial (bf16 as well: the merge takes it back to
+    // fp32 and weights it)
+    const bool final_out = nsplit == 1;
+    for (int hr = wave_all; hr < C::HG; hr += W * kHalves) {
+      const int head = head_base + hr;
+      if (head < p.h_q) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(stage + hr * kStageRow + 16 * lane);
+        uint16_t* const dst = final_out ? p.out + ((int64_t)row * p.h_q + head) * kHeadDim
+                                        : static_cast<uint16_t*>(p.part_o) + ((int64_t)slot * p.h_q + head) * kHeadDim;
+        *reinterpret_cast<u32x4*>(dst + 8 * lane) = v;
       }
     }
     const int head_e = head_base + 16 * wave + t16e;

@@ -191,8 +191,8 @@ void sparse_decode_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(16))) char lds[kHalves * (C::kLdsBytes + kRawHalfBytes)];
   // epilogue staging of the bf16 output rows (16 bytes of padding per 1 KB row)
   constexpr int kStageRow = 2 * kHeadDim + 16;
-  static_assert(C::kLdsBytes + C::HG * kStageRow <= kHalves * (C::kLdsBytes + kRawHalfBytes),
-                "the output staging fits in the workgroup's LDS past half 0's area");
+  static_assert(C::HG * kStageRow <= kMergeOBytes, "the output staging reuses the O exchange area");
+  static_assert(C::kHB == kHalves, "each half keeps one 32-head O block");
 
   // The wave index is uniform: keep it (and everything derived from it) in scalar registers.
   // Half h (waves hW .. hW+W-1) takes the sub-tiles s = h (mod 2) of the part, with its own LDS
@@ -207,7 +207,6 @@ void sparse_decode_kernel(DecodeParams p) {
   char* vslice = smem + C::kOffV + wave * C::kVBytes;
   char* pbuf = smem + C::kOffP;
   float* alpha_s = reinterpret_cast<float*>(smem + C::kOffAlpha);
-  float* lfin_s = reinterpret_cast<float*>(smem + C::kOffLFin);
   int* flag_s = reinterpret_cast<int*>(smem + C::kOffFlag);
 
   // This part's units run from (sc[0], sc[1]) to the exclusive end (sc[2], sc[3]); they are walked
@@ -502,80 +501,70 @@ void sparse_decode_kernel(DecodeParams p) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 
-    // ---------------- merge of the two halves (log-sum-exp): half 1 hands its running maximum and
-    // sum per head and its unnormalised O to half 0 through LDS; half 0 rescales both to the larger
-    // maximum and adds them. A half that saw no valid token (m = -inf) carries no weight.
-    {
-      float* const obuf = reinterpret_cast<float*>(lds);
-      float* const ml = reinterpret_cast<float*>(lds + kMergeOBytes);   // [half][m, l][head]
-      const int ln = lane_id();
-      const int t16m = ln & 15;
-      if ((ln >> 4) == 0) {
-        ml[(2 * half + 0) * C::HG + 16 * wave + t16m] = m_run;
-        ml[(2 * half + 1) * C::HG + 16 * wave + t16m] = l_run;
-      }
-      if (half == 1) {
-#pragma unroll
-        for (int d = 0; d < C::kDB; ++d)
-#pragma unroll
-          for (int b = 0; b < C::kHB; ++b)
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-              obuf[(((wave * C::kDB + d) * C::kHB + b) * 16 + r) * 64 + ln] = oacc[d][b][r];
-      }
-      __syncthreads();
-      if (half == 0) {
-        const float ninf = -__builtin_inff();
-        auto weights = [&](int hl, float& a0, float& a1, float& m) {
-          const float m0 = ml[0 * C::HG + hl], m1 = ml[2 * C::HG + hl];
-          m = fmaxf(m0, m1);
-          a0 = m0 == ninf ? 0.0f : __builtin_amdgcn_exp2f(m0 - m);
-          a1 = m1 == ninf ? 0.0f : __builtin_amdgcn_exp2f(m1 - m);
-        };
-#pragma unroll
-        for (int b = 0; b < C::kHB; ++b) {
-          float a0, a1, m;
-          weights(32 * b + (ln & 31), a0, a1, m);
-#pragma unroll
-          for (int d = 0; d < C::kDB; ++d)
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-              oacc[d][b][r] = a0 * oacc[d][b][r] +
-                              a1 * obuf[(((wave * C::kDB + d) * C::kHB + b) * 16 + r) * 64 + ln];
-        }
-        float a0, a1, m;
-        const int hs = 16 * wave + t16m;              // this lane's softmax head
-        weights(hs, a0, a1, m);
-        l_run = a0 * ml[1 * C::HG + hs] + a1 * ml[3 * C::HG + hs];
-        m_run = m;
-      }
-      __syncthreads();
-    }
-
-    // ---------------- epilogue for this row segment. Half 0 normalises O and stages it in bf16 in
-    // LDS (head rows kStageRow bytes apart, past half 0's area); then every wave stores whole 1 KB
-    // head rows, 16 bytes per lane, instead of 16 bytes into each of 32 rows per store instruction.
+    // ---------------- merge of the two halves (log-sum-exp) and staging of the output. Half h keeps
+    // the 32-head O block h and hands its other block to the other half through LDS, with its
+    // running maximum and sum per head. Each half then rescales both contributions to its heads to
+    // the larger maximum, adds them, normalises by the combined sum and stages the result in bf16
+    // in LDS (head rows kStageRow bytes apart). A half that saw no valid token (m = -inf) carries
+    // no weight.
     lane = lane_id();
     const int t16e = lane & 15, q4e = lane >> 4, hhe = lane >> 5;
-    if (half == 0 && q4e == 0) lfin_s[16 * wave + t16e] = l_run;
-    __syncthreads();
-    char* const stage = lds + C::kLdsBytes;
+    float* const xbuf = reinterpret_cast<float*>(lds);                 // [to half][wave][d][r][lane]
+    float* const ml = reinterpret_cast<float*>(lds + kMergeOBytes);   // [half][m, l][head]
+    char* const stage = lds;                                           // after xbuf is consumed
+    auto xoff = [&](int to, int d, int r) { return (((to * W + wave) * C::kDB + d) * 16 + r) * 64 + lane; };
+    if (q4e == 0) {
+      ml[(2 * half + 0) * C::HG + 16 * wave + t16e] = m_run;
+      ml[(2 * half + 1) * C::HG + 16 * wave + t16e] = l_run;
+    }
     if (half == 0) {
 #pragma unroll
-      for (int b = 0; b < C::kHB; ++b) {
-        const int hl = 32 * b + (lane & 31);
-        const float l = lfin_s[hl];
-        const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+      for (int d = 0; d < C::kDB; ++d)
 #pragma unroll
-        for (int d = 0; d < C::kDB; ++d) {
+        for (int r = 0; r < 16; ++r) xbuf[xoff(1, d, r)] = oacc[d][1][r];
+    } else {
 #pragma unroll
-          for (int jb = 0; jb < 4; ++jb) {
-            const int dim = wave * C::kSlice + 32 * d + 8 * jb + 4 * hhe;
-            bf16x4 o;
+      for (int d = 0; d < C::kDB; ++d)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) o[i] = (__bf16)(oacc[d][b][4 * jb + i] * inv);
-            *reinterpret_cast<bf16x4*>(stage + hl * kStageRow + 2 * dim) = o;
-          }
+        for (int r = 0; r < 16; ++r) xbuf[xoff(0, d, r)] = oacc[d][0][r];
+    }
+    __syncthreads();
+    const float ninf = -__builtin_inff();
+    // combined weights of head hl: a_h = 2^(m_h - m) / l with m the larger maximum and l the
+    // combined sum (0 for a half without a valid token, and for both when the head saw none)
+    auto weights = [&](int hl, float& a0, float& a1, float& m, float& l) {
+      const float m0 = ml[0 * C::HG + hl], m1 = ml[2 * C::HG + hl];
+      m = fmaxf(m0, m1);
+      a0 = m0 == ninf ? 0.0f : __builtin_amdgcn_exp2f(m0 - m);
+      a1 = m1 == ninf ? 0.0f : __builtin_amdgcn_exp2f(m1 - m);
+      l = a0 * ml[1 * C::HG + hl] + a1 * ml[3 * C::HG + hl];
+      const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+      a0 *= inv;
+      a1 *= inv;
+    };
+    {
+      const int hl = 32 * half + (lane & 31);
+      float a0, a1, m, l;
+      weights(hl, a0, a1, m, l);
+      const float a_own = half == 0 ? a0 : a1, a_other = half == 0 ? a1 : a0;
+      f32x16 on[C::kDB];
+#pragma unroll
+      for (int d = 0; d < C::kDB; ++d)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float own = half == 0 ? oacc[d][0][r] : oacc[d][1][r];
+          on[d][r] = a_own * own + a_other * xbuf[xoff(half, d, r)];
+        }
+      __syncthreads();                          // xbuf is read by everyone before the staging
+#pragma unroll
+      for (int d = 0; d < C::kDB; ++d) {
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb) {
+          const int dim = wave * C::kSlice + 32 * d + 8 * jb + 4 * hhe;
+          bf16x4 o;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) o[i] = (__bf16)on[d][4 * jb + i];
+          *reinterpret_cast<bf16x4*>(stage + hl * kStageRow + 2 * dim) = o;
         }
       }
     }
@@ -592,10 +581,12 @@ void sparse_decode_kernel(DecodeParams p) {
         *reinterpret_cast<u32x4*>(dst + 8 * lane) = v;
       }
     }
-    const int head_e = head_base + 16 * wave + t16e;
+    const int hs = 16 * wave + t16e;
+    const int head_e = head_base + hs;
     if (half == 0 && q4e == 0 && head_e < p.h_q) {
-      const float lse = l_run > 0.0f ? (m_run + __log2f(l_run)) * 0.69314718055994530942f
-                                     : -__builtin_inff();
+      float a0, a1, m, l;
+      weights(hs, a0, a1, m, l);
+      const float lse = l > 0.0f ? (m + __log2f(l)) * 0.69314718055994530942f : -__builtin_inff();
       if (final_out)
         p.lse[(int64_t)row * p.h_q + head_e] = lse;
       else

@@ -381,18 +381,31 @@ void sparse_decode_kernel(DecodeParams p) {
         // ---------------- QK^T from the bf16 tile: S^T[32 tokens x 16 heads] in two token blocks.
         // Step (c, h) multiplies dims 64c + 16*q4 + 8h .. +7 of token 16tb + t16 (slice c/2 of the
         // tile) with the same dims of Q.
+        // The four K operands of step c + 1 are read before the four MFMAs of step c, and the two
+        // token blocks alternate, so that neither an LDS read nor the previous MFMA on the same
+        // accumulator is waited for right before each MFMA.
         f32x4 sacc[2] = {f32x4{}, f32x4{}};
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
+        auto read_k = [&](int c, bf16x8 (&kb)[4]) {
           const char* kslice = smem + C::kOffV + (c >> 1) * C::kVBytes + ((c & 1) * 64 + 16 * q4) * 2;
 #pragma unroll
           for (int tb = 0; tb < 2; ++tb) {
             const char* kp = kslice + (16 * tb + t16) * C::kVStride;
-            const bf16x8 a0 = __builtin_bit_cast(bf16x8, lds_read16(kp, 0));
-            const bf16x8 a1 = __builtin_bit_cast(bf16x8, lds_read16(kp, 16));
-            sacc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qreg[c][0], sacc[tb], 0, 0, 0);
-            sacc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qreg[c][1], sacc[tb], 0, 0, 0);
+            kb[2 * tb] = __builtin_bit_cast(bf16x8, lds_read16(kp, 0));
+            kb[2 * tb + 1] = __builtin_bit_cast(bf16x8, lds_read16(kp, 16));
           }
+        };
+        bf16x8 kbuf[2][4];
+        read_k(0, kbuf[0]);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          if (c + 1 < 8) read_k(c + 1, kbuf[(c + 1) & 1]);
+          __builtin_amdgcn_sched_barrier(0);         // keep those reads ahead of these MFMAs
+          const bf16x8 (&kb)[4] = kbuf[c & 1];
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int tb = 0; tb < 2; ++tb)
+              sacc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[2 * tb + h], qreg[c][h], sacc[tb], 0, 0, 0);
         }
 
         // ---------------- online softmax for head 16*wave + t16; sacc[tb][i] is token 16tb+4q4+i

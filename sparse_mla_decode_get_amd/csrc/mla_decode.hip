@@ -205,6 +205,13 @@ void sparse_decode_kernel(DecodeParams p) {
   const int head_base = blockIdx.y * C::HG;
 
   char* vslice = smem + C::kOffV + wave * C::kVBytes;
+  // Q staging at a row segment's start: head row hr (bf16, 1 KB) in the tile area of half hr / 32
+  // at (hr % 32) * kQRow bytes; the 16-byte padding keeps 16 rows at one offset on distinct banks.
+  constexpr int kQRow = 2 * kHeadDim + 16;
+  static_assert(32 * kQRow <= W * C::kVBytes && C::HG == 64, "the Q staging fits in the tile areas");
+  auto q_row = [&](int hr) -> char* {
+    return lds + (hr >> 5) * C::kLdsBytes + C::kOffV + (hr & 31) * kQRow;
+  };
   char* pbuf = smem + C::kOffP;
   float* alpha_s = reinterpret_cast<float*>(smem + C::kOffAlpha);
   int* flag_s = reinterpret_cast<int*>(smem + C::kOffFlag);
@@ -233,17 +240,17 @@ void sparse_decode_kernel(DecodeParams p) {
 
     // Q (B operand): heads past h_q load a copy of the last head; their results are never stored.
     // Q (B operand): heads past h_q load a copy of the last head; their results are never stored.
-    bf16x8 qreg[8][2];
-    {
-      const int qh = min(my_head, p.h_q - 1);
-      const u32x4* qp = reinterpret_cast<const u32x4*>(
-          p.q + ((int64_t)row * p.h_q + qh) * kHeadDim + 16 * q4);
+    // Q rows of the workgroup's heads are copied once into LDS (8 head rows of 1 KB per wave, row
+    // hr of half hr / 32's tile area at (hr % 32) * kQRow, free until the first dequantization) and
+    // read into registers from there below, instead of every half loading all of Q from memory.
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        qreg[c][0] = __builtin_bit_cast(bf16x8, qp[8 * c]);
-        qreg[c][1] = __builtin_bit_cast(bf16x8, qp[8 * c + 1]);
-      }
+    for (int i = 0; i < 8; ++i) {
+      const int hr = 8 * wave_all + i;
+      const int qh = min(head_base + hr, p.h_q - 1);
+      const uint16_t* src = p.q + ((int64_t)row * p.h_q + qh) * kHeadDim + 8 * lane;
+      copy16_to_lds(src, __builtin_amdgcn_readfirstlane(lds_addr(q_row(hr))));
     }
+    bf16x8 qreg[8][2];
 
     f32x16 oacc[C::kDB][C::kHB];
 #pragma unroll
@@ -316,6 +323,18 @@ void sparse_decode_kernel(DecodeParams p) {
     for (int k = 0; k < kDepth; ++k) load_idx(k);
     // vmcnt(0) as a compiler-visible wait, so Q counts as resident for the rest of the segment
     __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();                                  // every wave's Q rows are in LDS
+    {
+      // lane (t16, q4) takes dims 64c + 16*q4 .. +15 of head my_head
+      const char* qrow = q_row(16 * wave + t16) + 32 * q4;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        qreg[c][0] = __builtin_bit_cast(bf16x8, lds_read16(qrow, 128 * c));
+        qreg[c][1] = __builtin_bit_cast(bf16x8, lds_read16(qrow, 128 * c + 16));
+      }
+      // complete before any wave can reach the first dequantization, which overwrites these rows
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    }
     uint32_t mk[kDepth + 1];                          // validity masks of iterations k .. k+kDepth
 #pragma unroll
     for (int k = 0; k < kDepth; ++k) {

@@ -12,7 +12,8 @@
 // (HG = 64 here). The workgroup is two halves of W = HG / 16 = 4 waves (eight waves, two per SIMD,
 // one workgroup per CU); half h takes the sub-tiles s = h (mod 2) of the part with its own LDS
 // areas, and the halves' softmax states are merged by log-sum-exp at the end of each row segment.
-// Every wave has the same register footprint: Q of 16 heads (64 VGPRs) and an fp32 output
+// Every wave has the same register footprint: Q of 16 heads (64 VGPRs; each head's row is copied
+// once per workgroup into LDS at a row segment's start and read from there) and an fp32 output
 // accumulator of 8 MFMA blocks. Each 64-slot unit runs as two sub-tiles of 32 tokens:
 //   1. indices  each wave copies the sub-tile's 32 index entries into its LDS index ring
 //               (global_load_lds_dword), 2 * kDepth sub-tiles ahead of the compute.
@@ -36,11 +37,13 @@
 //   6. PV       wave w accumulates O^T[its dim slice x all HG heads] += V^T P^T with
 //               v_mfma_f32_32x32x16_bf16; V^T comes from its own tile slice via ds_read_b64_tr_b16,
 //               P^T from LDS.
-//   7. merge    half 1 passes its per-head maximum and sum and its unnormalised O to half 0 through
-//               LDS; half 0 rescales both to the larger maximum and adds them.
-//   8. epilogue one split: out = O / l in bf16 and lse = ln(2) * (m + log2 l); several splits: the
-//               normalised partial (bf16) and its lse (fp32) go to the workspace for the merge
-//               kernel.
+//   7. merge    half h keeps the 32-head O block h and passes the other block, with its per-head
+//               maximum and sum, to the other half through LDS; each half rescales both
+//               contributions to its heads to the larger maximum, adds them and normalises.
+//   8. epilogue the normalised rows are staged in bf16 in LDS and stored as whole 1 KB head rows by
+//               all eight waves. One split: out = O / l in bf16 and lse = ln(2) * (m + log2 l);
+//               several splits: the normalised partial (bf16) and its lse (fp32) go to the
+//               workspace for the merge kernel.
 
 #include "mla_device.h"
 #include "mla_internal.h"

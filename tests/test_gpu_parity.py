@@ -150,6 +150,10 @@ def test_decode_small_default_schedule(spec):
     (Spec("split_h16", 1, 1, 16, 1000, 4096, neg="frac5"), 16, 1),
     (Spec("one_part", 3, 2, 128, 150, 2048), 1, 1),
     (Spec("split_empty_rows", 2, 1, 64, 500, 2048, neg="all"), 4, 1),
+    # 64-head kernel with heads 40..63 of its group past h_q, and four parts of 9 units over six
+    # rows of 6: each part runs several row segments (staging Q again at the start of every one)
+    # and some rows are split
+    (Spec("h40_multi_segment", 3, 2, 40, 333, 2048, neg="frac5"), 4, 1),
 ], ids=lambda x: x.name if isinstance(x, Spec) else str(x))
 def test_decode_split_rows(spec, parts, min_tiles):
     w = make_workload(spec, seed=11)

@@ -3,8 +3,11 @@
 One step = one mla_sparse_decode call over one batch of synthetic input already resident in HBM
 (the decode kernel, plus the log-sum-exp merge kernel when the schedule splits rows); the tile
 scheduler metadata is computed once before the loop, as the method prescribes, and timed separately.
-Successive steps cycle through several independent index sets over the same paged pool, so no step
-re-reads the records of the previous one from cache.
+Successive steps cycle through independent index sets over the same paged pool, enough of them that
+the records one cycle selects exceed 512 MiB: by the time a set comes round again, its records have
+been pushed out of L2 and the 256 MiB Infinity Cache by the other sets' traffic, so the timed steps
+read their records from HBM. The long workload selects every token of its 553 MB pool in order, a
+stream larger than the Infinity Cache, and uses one set.
 
 Prints one JSON line: TFLOP/s over valid selected tokens (2 * h_q * (512 + 512) flops per valid
 token and row), KV GB/s, the roofline block for the decode kernel, and the CPU oracle baseline.
@@ -80,13 +83,15 @@ def cpu_baseline(w, seconds: float):
         kv += 528.0 * nv + 288.0 * nx
         done += 1
     dt = time.perf_counter() - t0
+    cores = len(os.sched_getaffinity(0))
     try:
         import threadpoolctl
-        threads = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()) \
-            if threadpoolctl.threadpool_info() else 1
+        info = threadpoolctl.threadpool_info()
+        blas = max(i.get("num_threads", 1) for i in info) if info else 1
     except Exception:
-        threads = len(os.sched_getaffinity(0))
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+        blas = None
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "blas_threads": blas,
+            "kind": "oracle",
             "sample": f"{done} of {rows} query rows of the same workload (all {spec.h_q} heads each), "
                       f"{dt:.1f} s wall, float64 NumPy oracle on the host; KV {kv / dt / 1e9:.3f} GB/s"}
 
@@ -97,7 +102,9 @@ def main():
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--config", type=int, default=2)
-    ap.add_argument("--sets", type=int, default=4, help="independent index sets cycled over steps")
+    ap.add_argument("--sets", type=int, default=0,
+                    help="independent index sets cycled over steps (0: enough that one cycle "
+                         "selects more than 512 MiB of records, at least 4)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-probe", action="store_true",
@@ -111,7 +118,7 @@ def main():
     import torch
 
     import sparse_mla_decode_get_amd as mla
-    from workloads import CONFIGS, add_index_set, make_workload
+    from workloads import CONFIGS, add_extra_index_set, add_index_set, make_workload
 
     mla.load_library()          # fails loudly when the HIP library is missing
     dev = torch.device("cuda", 0)
@@ -120,8 +127,15 @@ def main():
     t_gen = time.perf_counter()
     w = make_workload(args.config)
     spec = w["spec"]
-    sets = [w["indices"]] + [add_index_set(w, 5000 + k) for k in range(args.sets - 1)] \
-        if spec.extra_topk == 0 and spec.order == "random" else [w["indices"]]
+    set_kv = 528.0 * (w["indices"] >= 0).sum() + (
+        0.0 if w["extra_indices"] is None else 288.0 * (w["extra_indices"] >= 0).sum())
+    n_sets = args.sets or max(4, int(np.ceil(512 * 2**20 / set_kv)) + 1)
+    if spec.order != "random":
+        n_sets = 1
+    sets = [w["indices"]] + [add_index_set(w, 5000 + k) for k in range(n_sets - 1)]
+    xsets = None
+    if w["extra_indices"] is not None:
+        xsets = [w["extra_indices"]] + [add_extra_index_set(w, 7000 + k) for k in range(n_sets - 1)]
     t_gen = time.perf_counter() - t_gen
 
     if args.copy_probe:
@@ -134,10 +148,11 @@ def main():
     q = torch.from_numpy(w["q_bits"].view(np.int16)).view(torch.bfloat16).to(dev)
     k_cache = torch.from_numpy(w["k_cache"]).to(dev)
     idx_sets = [torch.from_numpy(s).to(dev) for s in sets]
-    xc = xi = None
+    xc = None
+    xidx_sets = [None] * len(sets)
     if w["extra_k_cache"] is not None:
         xc = torch.from_numpy(w["extra_k_cache"]).to(dev)
-        xi = torch.from_numpy(w["extra_indices"]).to(dev)
+        xidx_sets = [torch.from_numpy(s).to(dev) for s in xsets]
     b, s, h = spec.batch, spec.seq_len_q, spec.h_q
     out = torch.empty((b, s, h, 512), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((b, s, h), dtype=torch.float32, device=dev)
@@ -152,7 +167,8 @@ def main():
     metadata_ms = e0.elapsed_time(e1)
 
     def step(k):
-        mla.sparse_decode(q, k_cache, idx_sets[k % len(idx_sets)], w["softmax_scale"], md, xc, xi,
+        j = k % len(idx_sets)
+        mla.sparse_decode(q, k_cache, idx_sets[j], w["softmax_scale"], md, xc, xidx_sets[j],
                           out=out, lse=lse)
 
     for k in range(args.warmup):
@@ -176,7 +192,8 @@ def main():
 
     # algorithmic work per step (valid tokens only), averaged over the index sets the steps used
     nv = np.mean([[(sets[k % len(sets)] >= 0).sum()] for k in range(args.steps)])
-    nx = 0 if w["extra_indices"] is None else float((w["extra_indices"] >= 0).sum())
+    nx = 0 if xsets is None else np.mean([[(xsets[k % len(xsets)] >= 0).sum()]
+                                          for k in range(args.steps)])
     flops = 2.0 * h * 1024 * (nv + nx)
     kv_bytes = 528.0 * nv + 288.0 * nx
     rows = b * s
@@ -194,6 +211,24 @@ def main():
                 "peak": HBM_PEAK_GBS, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = stored_traffic(args.config, h > 64)
+
+    # measured HBM bandwidth of a plain 1 GiB device-to-device copy (read + write bytes over time),
+    # reported beside the 8 TB/s spec; taken after the timed region
+    copy_gbs = None
+    if not args.copy_probe:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 10
+        c0.record()
+        for _ in range(reps):
+            dst.copy_(src)
+        c1.record()
+        torch.cuda.synchronize()
+        copy_gbs = 2.0 * src.numel() * reps / (c0.elapsed_time(c1) * 1e-3) / 1e9
+        del src, dst
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -223,6 +258,8 @@ def main():
         "alg_gbps": alg_bytes / (ms_per_step * 1e-3) / 1e9,
         "valid_tokens_per_step": float(nv + nx),
         "hbm_frac": alg_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "hbm_copy_gbps_measured": copy_gbs,
+        "index_set_mib_per_cycle": len(sets) * set_kv / 2**20,
         "metadata_ms": metadata_ms,
         "per_launch_ms": per_launch_ms,
         "wall_s_timed": wall,

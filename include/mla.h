@@ -46,7 +46,7 @@ typedef enum {
   MLA_ERR_INVALID_ARG = -1,   /* null pointer, bad shape, misaligned buffer, inconsistent arguments */
   MLA_ERR_UNSUPPORTED = -2,   /* shape outside what the kernels implement (e.g. head_dim != 512) */
   MLA_ERR_WORKSPACE = -3,     /* workspace missing or smaller than mla_workspace_bytes() */
-  MLA_ERR_INDEX_RANGE = -4,   /* reserved for index range failures reported by helpers */
+  MLA_ERR_INDEX_RANGE = -4,   /* mla_check_indices found an index at or past the cache size */
   MLA_ERR_HIP = -5            /* a HIP runtime call or kernel launch failed */
 } mla_status;
 
@@ -108,7 +108,9 @@ size_t mla_workspace_bytes(int batch, int seq_len_q, int h_q, int topk, int extr
  *                  intensity"); 16-byte aligned.
  *   extra_indices  NULL, or device int32 [batch][seq_len_q][extra_topk] into extra_k_cache.
  *                  Each row attends with ONE softmax over the union of both selections.
- *   softmax_scale  multiplier of q.k before the softmax (e.g. 1/sqrt(512)).
+ *   softmax_scale  multiplier of q.k before the softmax (e.g. 1/sqrt(512)); must be finite and
+ *                  > 0 (MLA_ERR_INVALID_ARG otherwise). The scaled scores are computed in fp32, so
+ *                  |softmax_scale * q.k| must stay within fp32 range, like the cache values'.
  *   sched, split_ptr, num_parts_used  the metadata from mla_get_metadata for the same
  *                  (batch, seq_len_q, h_q, topk, extra_topk).
  *   workspace      device buffer, 256-byte aligned, of workspace_bytes >= mla_workspace_bytes(...)
@@ -154,6 +156,17 @@ int mla_dequant_records(const uint8_t* cache, int record_bytes, const int32_t* i
  */
 int mla_validate_indices(const int32_t* idx, int64_t n, int64_t num_tokens, int32_t* bad_count,
                          void* stream);
+
+/*
+ * Debug helper, blocking form of mla_validate_indices: runs the same count into bad_count (device
+ * int32), waits for `stream`, and returns MLA_OK when every entry is < num_tokens (negative entries
+ * are ignored entries and always pass) or MLA_ERR_INDEX_RANGE when some entry is out of the cache.
+ * Out-of-cache indices are a precondition violation of mla_sparse_decode (page "deepseek-ai/FlashMLA",
+ * section "Key technical details": entries select KV pages, -1 marks the ignored ones); this call
+ * lets a caller test that precondition off the hot path.
+ */
+int mla_check_indices(const int32_t* idx, int64_t n, int64_t num_tokens, int32_t* bad_count,
+                      void* stream);
 
 #ifdef __cplusplus
 }

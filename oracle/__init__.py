@@ -14,6 +14,9 @@ Everything here is plain, slow and float64, written from the pages' own statemen
                    section "Workarounds"; page "deepseek-ai/FlashMLA", section "How to use it").
 * ``metadata``  -- the tile-scheduler partition computed once before the decode loop (same sections).
                    The pages give only its existence, so its content is this package's own spec.
+* ``encode``    -- the cache writer: bf16 latents -> 528 B fp8 / 288 B fp4 records (page
+                   "flops/flashmla-decode-fp8-fp4-kv", section "Arithmetic intensity"); the pages
+                   fix the layout, the scale choice is this package's reading (see that module).
 
 Parity status: every function is pinned by the ``-m "not gpu"`` tests in ``tests/test_oracle_*.py``
 against library decoders, closed forms, invariants and hand-derived fixtures under ``tests/golden/``.
@@ -23,10 +26,13 @@ from .formats import (E2M1, E4M3, E8M0, FP4_RECORD_BYTES, FP8_RECORD_BYTES, HEAD
 from .attention import (oracle_combine, oracle_decode, oracle_decode_rows, oracle_split_decode,
                         row_token_lists)
 from .metadata import TILE_TOKENS, oracle_metadata, part_count, tiles_per_row
+from .encode import (e2m1_encode, e4m3_encode, encode_fp4_records, encode_fp8_records,
+                     fp8_scale_exponent)
 
 __all__ = [
     "E2M1", "E4M3", "E8M0", "FP4_RECORD_BYTES", "FP8_RECORD_BYTES", "HEAD_DIM", "TILE_TOKENS",
     "bf16_bits_to_f64", "dequant_fp4_records", "dequant_fp8_records", "oracle_combine",
     "oracle_decode", "oracle_decode_rows", "oracle_metadata", "oracle_split_decode", "part_count",
-    "row_token_lists", "tiles_per_row",
+    "row_token_lists", "tiles_per_row", "e2m1_encode", "e4m3_encode", "encode_fp4_records",
+    "encode_fp8_records", "fp8_scale_exponent",
 ]

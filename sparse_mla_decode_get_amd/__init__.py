@@ -17,7 +17,8 @@ import torch
 
 __all__ = ["HEAD_DIM", "FP8_RECORD_BYTES", "FP4_RECORD_BYTES", "TILE_TOKENS", "MLAError", "Metadata",
            "library_path", "load_library", "get_metadata", "workspace_bytes", "sparse_decode",
-           "combine", "dequant_records", "validate_indices", "metadata_parts", "error_string"]
+           "combine", "dequant_records", "validate_indices", "check_indices", "metadata_parts",
+           "error_string"]
 
 HEAD_DIM = 512
 FP8_RECORD_BYTES = 528
@@ -41,6 +42,7 @@ _SIG = {
     "mla_combine": (_I, [_VP, _VP, _VP, _I, _I, _VP, _VP, _VP]),
     "mla_dequant_records": (_I, [_VP, _I, _VP, _I, _VP, _VP]),
     "mla_validate_indices": (_I, [_VP, _I64, _I64, _VP, _VP]),
+    "mla_check_indices": (_I, [_VP, _I64, _I64, _VP, _VP]),
 }
 
 
@@ -240,3 +242,17 @@ def validate_indices(idx: torch.Tensor, num_tokens: int) -> int:
         _check("mla_validate_indices", lib.mla_validate_indices(
             _ptr(idx), idx.numel(), num_tokens, _ptr(bad), _stream(idx.device)))
     return int(bad.item())
+
+
+def check_indices(idx: torch.Tensor, num_tokens: int) -> bool:
+    """True when every entry of idx is below num_tokens (mla_check_indices; waits for the stream).
+    Returns False when the library reports MLA_ERR_INDEX_RANGE; other failures raise."""
+    lib = load_library()
+    _need(idx, torch.int32, "idx")
+    bad = torch.empty((1,), dtype=torch.int32, device=idx.device)
+    with torch.cuda.device(idx.device):
+        rc = lib.mla_check_indices(_ptr(idx), idx.numel(), num_tokens, _ptr(bad), _stream(idx.device))
+    if rc == -4:
+        return False
+    _check("mla_check_indices", rc)
+    return True

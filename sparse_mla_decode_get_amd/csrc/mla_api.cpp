@@ -44,11 +44,18 @@ int default_parts(int h_q) {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
+// Largest number of (row, unit) pairs: with at most kMaxParts parts, the partition's products
+// p * U and (u + 1) * P (host and metadata kernel) stay below 2^60.
+constexpr int64_t kMaxUnits = int64_t(1) << 40;
+constexpr int kMaxParts = 1 << 20;
+
 int check_shape(int batch, int seq_len_q, int h_q, int topk, int extra_topk) {
   if (batch < 0 || seq_len_q < 0 || h_q <= 0 || topk < 0 || extra_topk < 0) return MLA_ERR_INVALID_ARG;
   if ((int64_t)batch * seq_len_q > kMaxRows) return MLA_ERR_UNSUPPORTED;
   if (h_q > 4096) return MLA_ERR_UNSUPPORTED;
   if (topk > (1 << 28) || extra_topk > (1 << 28)) return MLA_ERR_UNSUPPORTED;
+  if ((int64_t)batch * seq_len_q * tiles_per_row(topk, extra_topk, nullptr) > kMaxUnits)
+    return MLA_ERR_UNSUPPORTED;
   return MLA_OK;
 }
 
@@ -68,7 +75,7 @@ int resolve_parts(int batch, int seq_len_q, int h_q, int topk, int extra_topk, i
   int64_t p = units / min_tiles_per_part;
   if (p > num_parts) p = num_parts;
   if (p < 1) p = 1;
-  if (p > (1 << 20)) return MLA_ERR_UNSUPPORTED;
+  if (p > kMaxParts) return MLA_ERR_UNSUPPORTED;
   *out = (int)p;
   return MLA_OK;
 }
@@ -157,7 +164,10 @@ int mla_sparse_decode(const void* q, const uint8_t* k_cache, int64_t k_tokens,
   if (!aligned(q, 16) || !aligned(out, 8) || !aligned(lse, 4) || !aligned(k_cache, 16) ||
       !aligned(extra_k_cache, 16) || !aligned(indices, 4) || !aligned(extra_indices, 4))
     return MLA_ERR_INVALID_ARG;
-  if (!std::isfinite(softmax_scale)) return MLA_ERR_INVALID_ARG;
+  // The scale must be positive and finite: the 128-head kernel takes the largest scaled score as
+  // the scaled largest raw score, and ignored entries carry a large negative raw score.
+  if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.0f)) return MLA_ERR_INVALID_ARG;
+  if (num_parts_used > kMaxParts) return MLA_ERR_INVALID_ARG;
   int tiles_k = 0;
   const int tiles = tiles_per_row(topk, extra_topk, &tiles_k);
   const bool split = any_split(rows, tiles, num_parts_used);
@@ -237,6 +247,18 @@ int mla_validate_indices(const int32_t* idx, int64_t n, int64_t num_tokens, int3
   if (n < 0 || num_tokens < 0 || !bad_count || (n > 0 && !idx)) return MLA_ERR_INVALID_ARG;
   return mla::launch_validate(idx, n, num_tokens, bad_count, (hipStream_t)stream) == 0 ? MLA_OK
                                                                                        : MLA_ERR_HIP;
+}
+
+int mla_check_indices(const int32_t* idx, int64_t n, int64_t num_tokens, int32_t* bad_count,
+                      void* stream) {
+  const int rc = mla_validate_indices(idx, n, num_tokens, bad_count, stream);
+  if (rc != MLA_OK) return rc;
+  int32_t bad = 0;
+  hipStream_t s = (hipStream_t)stream;
+  if (hipMemcpyAsync(&bad, bad_count, sizeof(bad), hipMemcpyDeviceToHost, s) != hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return MLA_ERR_HIP;
+  return bad == 0 ? MLA_OK : MLA_ERR_INDEX_RANGE;
 }
 
 }  // extern "C"

@@ -178,15 +178,6 @@ __device__ __forceinline__ bf16x8 lds_v(uint32_t a0, uint32_t a1) {
   return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-// 8 e4m3 values (two words) -> bf16 with an e8m0 scale (see dequant_fp8_16).
-__device__ __forceinline__ bf16x8 dequant_fp8_8(uint32_t w0, uint32_t w1, uint32_t scale_byte) {
-  const float s = __builtin_bit_cast(float, scale_byte << 23);
-  return cat4(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, s, false),
-              __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, s, true),
-              __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, s, false),
-              __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, s, true));
-}
-
 // Wait until at most n of this wave's vector memory operations are outstanding (and all of its
 // LDS operations are done), then synchronise the workgroup. n is wave-uniform.
 __device__ __forceinline__ void wait_and_barrier(int n) {
@@ -1201,8 +1192,13 @@ void sparse_decode_wide_kernel(DecodeParams p) {
       asm volatile("s_waitcnt vmcnt(0)\n\ts_nop 15\n\ts_nop 3" : "+a"(oacc[15]) :: "memory");
 
       // A second pass is needed when some head's probabilities relative to m_ref could have
-      // overflowed; the decision has to be the same for the whole workgroup.
-      if (pass > 0) break;
+      // overflowed; the decision has to be the same for the whole workgroup. After the second
+      // pass every wave waits here until all waves are done with the tile slots: the epilogue's
+      // staging area covers them, and another wave's last PV may still be reading its tile.
+      if (pass > 0) {
+        wait_and_barrier(0);
+        break;
+      }
       const bool any_big = __ballot(m_max > m_ref + kRefSlack) != 0;   // all lanes vote
       if (lane_id() == 0) redo_flags[wave] = any_big ? 1 : 0;
       wait_and_barrier(0);

@@ -30,24 +30,25 @@ __device__ __forceinline__ bf16x8 cat4(bf16x2 a, bf16x2 b, bf16x2 c, bf16x2 d) {
   return __builtin_shufflevector(ab, cd, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-// fp8 chunk -> bf16. `raw` holds 16 consecutive e4m3 values of one record (little-endian byte
-// order: element i in byte i); `scale_byte` is the e8m0 scale shared by them. gfx950's scaled
-// convert reads only the exponent field of its f32 scale operand and applies it as 2^(e - 127), so
-// placing the e8m0 byte in that field gives exactly x * 2^(byte - 127) rounded once to bf16
-// (exact whenever the product is representable, NaN for the e8m0 NaN byte 0xFF).
+// 8 e4m3 values (the words w0, w1: element i in byte i) -> bf16 with one e8m0 scale. gfx950's
+// scaled convert reads only the exponent field of its f32 scale operand and applies it as
+// 2^(e - 127), so placing the e8m0 byte in that field gives exactly x * 2^(byte - 127) rounded once
+// to bf16 (exact whenever the product is representable, NaN for the e8m0 NaN byte 0xFF). Both
+// decode kernels and the dequant probe run this routine.
+__device__ __forceinline__ bf16x8 dequant_fp8_8(uint32_t w0, uint32_t w1, uint32_t scale_byte) {
+  const float s = __builtin_bit_cast(float, scale_byte << 23);
+  return cat4(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, s, false),
+              __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, s, true),
+              __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, s, false),
+              __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, s, true));
+}
+
+// fp8 chunk -> bf16: `raw` holds 16 consecutive e4m3 values of one record, all sharing the e8m0
+// scale `scale_byte` (two dequant_fp8_8 halves).
 __device__ __forceinline__ void dequant_fp8_16(u32x4 raw, uint32_t scale_byte, bf16x8& lo,
                                                bf16x8& hi) {
-  const float s = __builtin_bit_cast(float, scale_byte << 23);
-  bf16x2 a0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[0], s, false);
-  bf16x2 a1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[0], s, true);
-  bf16x2 a2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[1], s, false);
-  bf16x2 a3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[1], s, true);
-  bf16x2 b0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[2], s, false);
-  bf16x2 b1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[2], s, true);
-  bf16x2 b2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[3], s, false);
-  bf16x2 b3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[3], s, true);
-  lo = cat4(a0, a1, a2, a3);
-  hi = cat4(b0, b1, b2, b3);
+  lo = dequant_fp8_8(raw[0], raw[1], scale_byte);
+  hi = dequant_fp8_8(raw[2], raw[3], scale_byte);
 }
 
 // e4m3 byte (low 8 bits of `b`) -> f32, exact.

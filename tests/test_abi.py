@@ -134,4 +134,25 @@ def test_host_checks_reject_bad_workspace_scale_and_alignment(lib):
     assert decode(ws_ptr=ws + 16) == -3                      # not 256-byte aligned
     assert decode(scale=float("inf")) == -1                  # MLA_ERR_INVALID_ARG
     assert decode(scale=float("nan")) == -1
+    assert decode(scale=0.0) == -1                           # the scale must be positive
+    assert decode(scale=-0.0) == -1
+    assert decode(scale=-0.04) == -1
+    assert decode(scale=-float("inf")) == -1
     assert decode(qp=q + 2) == -1                            # q not 16-byte aligned
+
+
+def test_shapes_whose_partition_could_overflow_are_refused(lib):
+    """rows * units_per_row is bounded (2^40) so that the partition's products p * U stay inside
+    int64 for every allowed part count; larger shapes are refused before any device work."""
+    out = ctypes.c_int(0)
+    # 2^24 rows x 2^22 units per row = 2^46 units
+    assert lib.mla_metadata_parts(1 << 24, 1, 16, 1 << 28, 0, 4, 1, ctypes.byref(out)) == -2
+    assert mla.workspace_bytes(1 << 24, 1, 16, 1 << 28, 0, 4) == 0
+    # just inside the bound: 2^24 rows x 2^16 units
+    assert lib.mla_metadata_parts(1 << 24, 1, 16, 1 << 22, 0, 4, 1, ctypes.byref(out)) == 0
+    assert out.value == 4
+
+
+def test_check_indices_argument_errors(lib):
+    assert lib.mla_check_indices(None, 4, 10, None, None) == -1
+    assert lib.mla_check_indices(None, -1, 10, 1 << 20, None) == -1

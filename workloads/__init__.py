@@ -230,3 +230,22 @@ def add_index_set(w: dict, seed: int, encode_chunk: int = 65536) -> np.ndarray:
         part = sel[a:a + encode_chunk]
         pool[part] = encode_fp8_records(_values(rng_c, part.size, spec.values))
     return idx.astype(np.int32).reshape(b_, s_, spec.topk)
+
+
+def add_extra_index_set(w: dict, seed: int, encode_chunk: int = 65536) -> np.ndarray:
+    """The same as add_index_set for the fp4 extra cache of workload `w`: new distinct positions in
+    each row's extra sequence, newly selected fp4 records encoded into w["extra_k_cache"] in place.
+    Returns the int32 [B, S, extra_topk] indices."""
+    spec = w["spec"]
+    b_, s_ = spec.batch, spec.seq_len_q
+    rng_t, rng_i, rng_c = [np.random.default_rng(x) for x in np.random.SeedSequence(seed).spawn(3)]
+    blocks_per_seq = -(-spec.extra_tokens_per_seq // BLOCK)
+    table = rng_t.permutation(b_ * blocks_per_seq).reshape(b_, blocks_per_seq)
+    phys = _select(rng_i, None, b_, s_, spec.extra_topk, spec.extra_tokens_per_seq, spec.order, table)
+    idx = _apply_neg(rng_i, phys, spec.neg)
+    pool = w["extra_k_cache"]
+    sel = np.unique(idx[idx >= 0])
+    for a in range(0, sel.size, encode_chunk):
+        part = sel[a:a + encode_chunk]
+        pool[part] = encode_fp4_records(_values(rng_c, part.size, spec.values))
+    return idx.astype(np.int32).reshape(b_, s_, spec.extra_topk)

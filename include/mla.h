@@ -40,6 +40,7 @@ extern "C" {
                                      scales (one per 16 values) */
 #define MLA_TILE_TOKENS 64        /* token slots per scheduling unit */
 #define MLA_SCHED_FIELDS 8        /* int32 fields per part in the schedule */
+#define MLA_NOALLOC_SCRATCH_BYTES (72u << 20)  /* fixed split scratch of mla_sparse_decode_noalloc */
 
 typedef enum {
   MLA_OK = 0,
@@ -47,7 +48,9 @@ typedef enum {
   MLA_ERR_UNSUPPORTED = -2,   /* shape outside what the kernels implement (e.g. head_dim != 512) */
   MLA_ERR_WORKSPACE = -3,     /* workspace missing or smaller than mla_workspace_bytes() */
   MLA_ERR_INDEX_RANGE = -4,   /* mla_check_indices found an index at or past the cache size */
-  MLA_ERR_HIP = -5            /* a HIP runtime call or kernel launch failed */
+  MLA_ERR_HIP = -5,           /* a HIP runtime call or kernel launch failed */
+  MLA_ERR_SCRATCH_LIMIT = -6  /* mla_sparse_decode_noalloc: the split partials would need more than
+                                 MLA_NOALLOC_SCRATCH_BYTES */
 } mla_status;
 
 /* Human-readable text for a status code (static storage, never NULL). */
@@ -127,6 +130,23 @@ int mla_sparse_decode(const void* q, const uint8_t* k_cache, int64_t k_tokens,
                       int seq_len_q, int h_q, float softmax_scale, const int32_t* sched,
                       const int32_t* split_ptr, int num_parts_used, void* workspace,
                       size_t workspace_bytes, void* out, float* lse, void* stream);
+
+/*
+ * mla_sparse_decode for callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation. Same arguments, checks, kernels and results
+ * as mla_sparse_decode, without the workspace: the split partials go to a fixed device array of
+ * MLA_NOALLOC_SCRATCH_BYTES (72 MiB) that the library holds on each device it runs on until the
+ * process ends. The call allocates nothing. A schedule whose partials need more than that
+ * (mla_workspace_bytes(...) > MLA_NOALLOC_SCRATCH_BYTES) is refused with MLA_ERR_SCRATCH_LIMIT
+ * before any device work. Calls on one device share the array: calls that overlap in time on one
+ * device (different streams, or several host threads) race and must be serialised by the caller.
+ */
+int mla_sparse_decode_noalloc(const void* q, const uint8_t* k_cache, int64_t k_tokens,
+                              const int32_t* indices, int topk, const uint8_t* extra_k_cache,
+                              int64_t extra_tokens, const int32_t* extra_indices, int extra_topk,
+                              int batch, int seq_len_q, int h_q, float softmax_scale,
+                              const int32_t* sched, const int32_t* split_ptr, int num_parts_used,
+                              void* out, float* lse, void* stream);
 
 /*
  * Log-sum-exp merge of split partials (the second half of split decoding, page

@@ -39,6 +39,8 @@ _SIG = {
     "mla_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I, _I, _I]),
     "mla_sparse_decode": (_I, [_VP, _VP, _I64, _VP, _I, _VP, _I64, _VP, _I, _I, _I, _I,
                                ctypes.c_float, _VP, _VP, _I, _VP, ctypes.c_size_t, _VP, _VP, _VP]),
+    "mla_sparse_decode_noalloc": (_I, [_VP, _VP, _I64, _VP, _I, _VP, _I64, _VP, _I, _I, _I, _I,
+                                       ctypes.c_float, _VP, _VP, _I, _VP, _VP, _VP]),
     "mla_combine": (_I, [_VP, _VP, _VP, _I, _I, _VP, _VP, _VP]),
     "mla_dequant_records": (_I, [_VP, _I, _VP, _I, _VP, _VP]),
     "mla_validate_indices": (_I, [_VP, _I64, _I64, _VP, _VP]),

@@ -90,7 +90,97 @@ bool any_split(int64_t rows, int tiles, int parts) {
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// Bytes per partial output value: the 64-head kernel writes bf16 partials (the merge takes them back
+// to fp32), the 128-head kernel fp32 ones (its registers leave no room for the conversion).
+size_t partial_elem_bytes(int h_q) { return wide_for(h_q) ? sizeof(float) : sizeof(uint16_t); }
+
+size_t split_workspace_bytes(int batch, int seq_len_q, int h_q, int num_parts_used) {
+  const size_t slots = (size_t)batch * seq_len_q + (size_t)num_parts_used - 1;
+  // partial outputs, then fp32 partial lse
+  return align256(slots * h_q * MLA_HEAD_DIM * partial_elem_bytes(h_q)) +
+         align256(slots * h_q * sizeof(float));
+}
+
+
 }  // namespace
+
+namespace mla {
+
+int sparse_decode(const DecodeCall& c, const WorkspaceSource& ws) {
+  const int batch = c.batch, seq_len_q = c.seq_len_q, h_q = c.h_q, topk = c.topk;
+  const int extra_topk = c.extra_topk, num_parts_used = c.num_parts_used;
+  int rc = check_shape(batch, seq_len_q, h_q, topk, extra_topk);
+  if (rc != MLA_OK) return rc;
+  const int rows = batch * seq_len_q;
+  if (rows == 0) return MLA_OK;
+  if (!c.q || !c.out || !c.lse || !c.sched || !c.split_ptr || num_parts_used < 1)
+    return MLA_ERR_INVALID_ARG;
+  if (topk > 0 && (!c.k_cache || !c.indices || c.k_tokens <= 0)) return MLA_ERR_INVALID_ARG;
+  if (extra_topk > 0 && (!c.extra_k_cache || !c.extra_indices || c.extra_tokens <= 0))
+    return MLA_ERR_INVALID_ARG;
+  if (!aligned(c.q, 16) || !aligned(c.out, 8) || !aligned(c.lse, 4) || !aligned(c.k_cache, 16) ||
+      !aligned(c.extra_k_cache, 16) || !aligned(c.indices, 4) || !aligned(c.extra_indices, 4))
+    return MLA_ERR_INVALID_ARG;
+  // The scale must be positive and finite: the 128-head kernel takes the largest scaled score as
+  // the scaled largest raw score, and ignored entries carry a large negative raw score.
+  if (!std::isfinite(c.softmax_scale) || !(c.softmax_scale > 0.0f)) return MLA_ERR_INVALID_ARG;
+  if (num_parts_used > kMaxParts) return MLA_ERR_INVALID_ARG;
+  int tiles_k = 0;
+  const int tiles = tiles_per_row(topk, extra_topk, &tiles_k);
+  const bool split = any_split(rows, tiles, num_parts_used);
+  void* part_o = nullptr;
+  float* part_lse = nullptr;
+  if (split) {
+    const size_t need = split_workspace_bytes(batch, seq_len_q, h_q, num_parts_used);
+    void* base = ws.caller_ptr;
+    if (ws.fixed_bytes > 0) {
+      // the fixed device array: checked against its size before the device is touched
+      if (need > ws.fixed_bytes) return MLA_ERR_SCRATCH_LIMIT;
+      base = ws.fixed_ptr();
+      if (!base) return MLA_ERR_HIP;
+    } else if (!base || ws.caller_bytes < need || !aligned(base, 256)) {
+      return MLA_ERR_WORKSPACE;
+    }
+    const size_t slots = (size_t)rows + (size_t)num_parts_used - 1;
+    part_o = base;
+    part_lse = reinterpret_cast<float*>(static_cast<char*>(base) +
+                                        align256(slots * h_q * MLA_HEAD_DIM * partial_elem_bytes(h_q)));
+  }
+  DecodeParams p;
+  p.q = static_cast<const uint16_t*>(c.q);
+  p.kc = c.k_cache;
+  p.idx = c.indices;
+  p.xc = extra_topk > 0 ? c.extra_k_cache : nullptr;
+  p.xidx = extra_topk > 0 ? c.extra_indices : nullptr;
+  p.topk = topk;
+  p.extra_topk = extra_topk;
+  p.tiles_k = tiles_k;
+  p.tiles = tiles;
+  p.rows = rows;
+  p.h_q = h_q;
+  p.scale_log2 = c.softmax_scale * 1.4426950408889634f;
+  p.sched = c.sched;
+  p.split_ptr = c.split_ptr;
+  p.part_o = part_o;
+  p.part_lse = part_lse;
+  p.out = static_cast<uint16_t*>(c.out);
+  p.lse = c.lse;
+  hipStream_t s = (hipStream_t)c.stream;
+  const int launched = wide_for(h_q) ? launch_sparse_decode_wide(p, num_parts_used, head_groups(h_q), s)
+                                     : launch_sparse_decode(p, num_parts_used, head_groups(h_q), 4, s);
+  if (launched != 0) return MLA_ERR_HIP;
+  if (split) {
+    const int merged = wide_for(h_q)
+        ? launch_combine(static_cast<const float*>(part_o), part_lse, c.split_ptr, rows, h_q, p.out,
+                         c.lse, true, s)
+        : launch_combine_bf16(static_cast<const uint16_t*>(part_o), part_lse, c.split_ptr, rows,
+                              h_q, p.out, c.lse, s);
+    if (merged != 0) return MLA_ERR_HIP;
+  }
+  return MLA_OK;
+}
+
+}  // namespace mla
 
 extern "C" {
 
@@ -102,6 +192,9 @@ const char* mla_error_string(int code) {
     case MLA_ERR_WORKSPACE: return "workspace missing or too small";
     case MLA_ERR_INDEX_RANGE: return "index outside the cache";
     case MLA_ERR_HIP: return "HIP runtime or kernel launch failure";
+    case MLA_ERR_SCRATCH_LIMIT:
+      return "split partials need more than the fixed scratch array of mla_sparse_decode_noalloc "
+             "(MLA_NOALLOC_SCRATCH_BYTES); use mla_sparse_decode with a workspace";
     default: return "unknown mla status";
   }
 }
@@ -128,17 +221,6 @@ int mla_get_metadata(int batch, int seq_len_q, int h_q, int topk, int extra_topk
   return MLA_OK;
 }
 
-// Bytes per partial output value: the 64-head kernel writes bf16 partials (the merge takes them back
-// to fp32), the 128-head kernel fp32 ones (its registers leave no room for the conversion).
-static size_t partial_elem_bytes(int h_q) { return wide_for(h_q) ? sizeof(float) : sizeof(uint16_t); }
-
-static size_t split_workspace_bytes(int batch, int seq_len_q, int h_q, int num_parts_used) {
-  const size_t slots = (size_t)batch * seq_len_q + (size_t)num_parts_used - 1;
-  // partial outputs, then fp32 partial lse
-  return align256(slots * h_q * MLA_HEAD_DIM * partial_elem_bytes(h_q)) +
-         align256(slots * h_q * sizeof(float));
-}
-
 size_t mla_workspace_bytes(int batch, int seq_len_q, int h_q, int topk, int extra_topk,
                            int num_parts_used) {
   if (check_shape(batch, seq_len_q, h_q, topk, extra_topk) != MLA_OK || num_parts_used < 1) return 0;
@@ -153,66 +235,13 @@ int mla_sparse_decode(const void* q, const uint8_t* k_cache, int64_t k_tokens,
                       int seq_len_q, int h_q, float softmax_scale, const int32_t* sched,
                       const int32_t* split_ptr, int num_parts_used, void* workspace,
                       size_t workspace_bytes, void* out, float* lse, void* stream) {
-  int rc = check_shape(batch, seq_len_q, h_q, topk, extra_topk);
-  if (rc != MLA_OK) return rc;
-  const int rows = batch * seq_len_q;
-  if (rows == 0) return MLA_OK;
-  if (!q || !out || !lse || !sched || !split_ptr || num_parts_used < 1) return MLA_ERR_INVALID_ARG;
-  if (topk > 0 && (!k_cache || !indices || k_tokens <= 0)) return MLA_ERR_INVALID_ARG;
-  if (extra_topk > 0 && (!extra_k_cache || !extra_indices || extra_tokens <= 0))
-    return MLA_ERR_INVALID_ARG;
-  if (!aligned(q, 16) || !aligned(out, 8) || !aligned(lse, 4) || !aligned(k_cache, 16) ||
-      !aligned(extra_k_cache, 16) || !aligned(indices, 4) || !aligned(extra_indices, 4))
-    return MLA_ERR_INVALID_ARG;
-  // The scale must be positive and finite: the 128-head kernel takes the largest scaled score as
-  // the scaled largest raw score, and ignored entries carry a large negative raw score.
-  if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.0f)) return MLA_ERR_INVALID_ARG;
-  if (num_parts_used > kMaxParts) return MLA_ERR_INVALID_ARG;
-  int tiles_k = 0;
-  const int tiles = tiles_per_row(topk, extra_topk, &tiles_k);
-  const bool split = any_split(rows, tiles, num_parts_used);
-  void* part_o = nullptr;
-  float* part_lse = nullptr;
-  if (split) {
-    const size_t need = split_workspace_bytes(batch, seq_len_q, h_q, num_parts_used);
-    if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return MLA_ERR_WORKSPACE;
-    const size_t slots = (size_t)rows + (size_t)num_parts_used - 1;
-    part_o = workspace;
-    part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                        align256(slots * h_q * MLA_HEAD_DIM * partial_elem_bytes(h_q)));
-  }
-  mla::DecodeParams p;
-  p.q = static_cast<const uint16_t*>(q);
-  p.kc = k_cache;
-  p.idx = indices;
-  p.xc = extra_topk > 0 ? extra_k_cache : nullptr;
-  p.xidx = extra_topk > 0 ? extra_indices : nullptr;
-  p.topk = topk;
-  p.extra_topk = extra_topk;
-  p.tiles_k = tiles_k;
-  p.tiles = tiles;
-  p.rows = rows;
-  p.h_q = h_q;
-  p.scale_log2 = softmax_scale * 1.4426950408889634f;
-  p.sched = sched;
-  p.split_ptr = split_ptr;
-  p.part_o = part_o;
-  p.part_lse = part_lse;
-  p.out = static_cast<uint16_t*>(out);
-  p.lse = lse;
-  hipStream_t s = (hipStream_t)stream;
-  const int launched = wide_for(h_q) ? mla::launch_sparse_decode_wide(p, num_parts_used, head_groups(h_q), s)
-                                     : mla::launch_sparse_decode(p, num_parts_used, head_groups(h_q), 4, s);
-  if (launched != 0) return MLA_ERR_HIP;
-  if (split) {
-    const int merged = wide_for(h_q)
-        ? mla::launch_combine(static_cast<const float*>(part_o), part_lse, split_ptr, rows, h_q, p.out,
-                              lse, true, s)
-        : mla::launch_combine_bf16(static_cast<const uint16_t*>(part_o), part_lse, split_ptr, rows,
-                                   h_q, p.out, lse, s);
-    if (merged != 0) return MLA_ERR_HIP;
-  }
-  return MLA_OK;
+  const mla::DecodeCall c{q, k_cache, k_tokens, indices, topk, extra_k_cache, extra_tokens,
+                          extra_indices, extra_topk, batch, seq_len_q, h_q, softmax_scale, sched,
+                          split_ptr, num_parts_used, out, lse, stream};
+  mla::WorkspaceSource ws;
+  ws.caller_ptr = workspace;
+  ws.caller_bytes = workspace_bytes;
+  return mla::sparse_decode(c, ws);
 }
 
 int mla_combine(const float* partial, const float* partial_lse, const int32_t* split_ptr, int rows,

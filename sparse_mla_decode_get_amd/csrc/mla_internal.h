@@ -25,6 +25,40 @@ struct DecodeParams {
   float* lse;                // [rows][h_q]
 };
 
+// Arguments of one decode call, as the C entry points receive them (include/mla.h).
+struct DecodeCall {
+  const void* q;
+  const uint8_t* k_cache;
+  int64_t k_tokens;
+  const int32_t* indices;
+  int topk;
+  const uint8_t* extra_k_cache;
+  int64_t extra_tokens;
+  const int32_t* extra_indices;
+  int extra_topk;
+  int batch, seq_len_q, h_q;
+  float softmax_scale;
+  const int32_t* sched;
+  const int32_t* split_ptr;
+  int num_parts_used;
+  void* out;
+  float* lse;
+  void* stream;
+};
+
+// Where the split partials go: the caller's workspace (mla_sparse_decode), or, when fixed_bytes > 0,
+// the library's fixed device array of that size, whose address fixed_ptr() returns (nullptr on
+// failure) and which is looked up only once a call is known to need it and to fit.
+struct WorkspaceSource {
+  void* caller_ptr = nullptr;
+  size_t caller_bytes = 0;
+  size_t fixed_bytes = 0;
+  void* (*fixed_ptr)() = nullptr;
+};
+
+// Host checks, then the decode kernel and (for split rows) the merge on c.stream; an mla_status.
+int sparse_decode(const DecodeCall& c, const WorkspaceSource& ws);
+
 int launch_sparse_decode(const DecodeParams& p, int parts, int groups, int nw, hipStream_t stream);
 // 128-head groups, four waves of 32 heads each (mla_decode_wide.hip).
 int launch_sparse_decode_wide(const DecodeParams& p, int parts, int groups, hipStream_t stream);

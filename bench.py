@@ -96,6 +96,55 @@ def cpu_baseline(w, seconds: float):
                       f"{dt:.1f} s wall, float64 NumPy oracle on the host; KV {kv / dt / 1e9:.3f} GB/s"}
 
 
+def bench_quantize(args):
+    """The cache writer: one step quantizes `--tokens` bf16 latents (N(0,1) per 32-value block times
+    2^u, u ~ U(-4, 4)) into records scattered to random distinct token slots of a pool twice that
+    size. HBM-bound: each token reads 1024 B of bf16 and 4 B of slot and writes one record."""
+    import torch
+
+    import sparse_mla_decode_get_amd as mla
+    mla.load_library()
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    n, rec = args.tokens, args.record
+    rng = np.random.default_rng(77)
+    sets = []
+    for k in range(2):                     # two input sets alternate, each larger than the MALL
+        x = torch.randn((n, 512), dtype=torch.float32, generator=torch.Generator().manual_seed(k))
+        x = (x.view(n, 16, 32) * torch.exp2(torch.empty((n, 16, 1)).uniform_(-4, 4))).view(n, 512)
+        slots = torch.from_numpy(rng.permutation(2 * n)[:n].astype(np.int32))
+        sets.append((x.to(torch.bfloat16).to(dev), slots.to(dev)))
+    cache = torch.zeros((2 * n, rec), dtype=torch.uint8, device=dev)
+
+    def step(k):
+        x, slots = sets[k % 2]
+        mla.quantize_records(x, rec, cache=cache, slots=slots)
+
+    for k in range(args.warmup):
+        step(k)
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for k in range(args.steps):
+        step(k)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    alg = n * (1024.0 + 4.0 + rec)
+    gbs = alg / (ms * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": f"cache writer GB/s, bf16 -> {rec} B records", "value": gbs, "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"quantize {n} bf16 latents into {rec} B records at random slots of a "
+                               f"{2 * n}-token pool", "tokens": n, "record_bytes": rec},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": None},
+        "cpu_baseline": None}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -109,11 +158,18 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-probe", action="store_true",
                     help="run one 1 GiB device copy first (calibrates HBM byte counters)")
+    ap.add_argument("--op", choices=["decode", "quantize"], default="decode",
+                    help="decode (the hot path, default) or quantize (the cache writer)")
+    ap.add_argument("--tokens", type=int, default=1 << 20, help="--op quantize: tokens per step")
+    ap.add_argument("--record", type=int, default=528, help="--op quantize: 528 (fp8) or 288 (fp4)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
               "(rows shard across GPUs with no exchange; see DESIGN.md)", file=sys.stderr)
         sys.exit(2)
+    if args.op == "quantize":
+        bench_quantize(args)
+        return
 
     import torch
 

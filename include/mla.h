@@ -162,6 +162,28 @@ int mla_combine(const float* partial, const float* partial_lse, const int32_t* s
                 int h_q, void* out, float* lse, void* stream);
 
 /*
+ * Cache writer: quantize bf16 latents into the cache's per-token records (the step before decode).
+ *   x             device bf16 [n][512], 16-byte aligned: one latent per new token.
+ *   slots         NULL (row i is written to token i, n <= cache_tokens), or device int32 [n]: the
+ *                 flat token id (physical_block * block_size + offset) each row is written to;
+ *                 entries < 0 or >= cache_tokens write nothing.
+ *   record_bytes  528 (fp8 records) or 288 (fp4 records); cache device uint8 [cache_tokens][record],
+ *                 16-byte aligned.
+ * Layouts (page "flops/flashmla-decode-fp8-fp4-kv", section "Arithmetic intensity"; page
+ * "deepseek-ai/FlashMLA", section "Key technical details": quantized values first, then the
+ * token's scales): fp8 = 512 e4m3 values then 16 e8m0 scales, one per 32 values; fp4 = 256 bytes of
+ * e2m1 (even index in the low nibble) then 32 e4m3 scales, one per 16 values. The pages leave the
+ * choice of scales open; this library's rule: fp8 block with a = max|x|: scale 2^k with
+ * k = ceil(log2(a / 448)) clipped to [-127, 127] (k = 0 for an all-zero block), values rounded to the
+ * nearest e4m3 of x / 2^k, ties to even; fp4 block: scale = the nearest e4m3 of a / 6 (ties to even,
+ * saturating at 448; 1.0 when it rounds to 0), values the nearest e2m1 of x / scale (ties to even,
+ * saturating at +-6). Rounding keeps the sign. x must be finite. Distinct rows must not share a slot
+ * (the record written last is unspecified).
+ */
+int mla_quantize_records(const void* x, int64_t n, const int32_t* slots, int record_bytes,
+                         uint8_t* cache, int64_t cache_tokens, void* stream);
+
+/*
  * Diagnostic: dequantize whole records with the same device routine the decode kernel uses.
  *   cache         device uint8 records of record_bytes (528 = fp8, 288 = fp4); 16-byte aligned.
  *   idx           device int32 [n] token ids (all must be >= 0 and inside the cache).

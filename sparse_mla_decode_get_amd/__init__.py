@@ -17,7 +17,8 @@ import torch
 
 __all__ = ["HEAD_DIM", "FP8_RECORD_BYTES", "FP4_RECORD_BYTES", "TILE_TOKENS", "MLAError", "Metadata",
            "library_path", "load_library", "get_metadata", "workspace_bytes", "sparse_decode",
-           "combine", "dequant_records", "validate_indices", "check_indices", "metadata_parts",
+           "combine", "dequant_records", "validate_indices", "check_indices", "quantize_records",
+           "metadata_parts",
            "error_string"]
 
 HEAD_DIM = 512
@@ -45,6 +46,7 @@ _SIG = {
     "mla_dequant_records": (_I, [_VP, _I, _VP, _I, _VP, _VP]),
     "mla_validate_indices": (_I, [_VP, _I64, _I64, _VP, _VP]),
     "mla_check_indices": (_I, [_VP, _I64, _I64, _VP, _VP]),
+    "mla_quantize_records": (_I, [_VP, _I64, _VP, _I, _VP, _I64, _VP]),
 }
 
 
@@ -258,3 +260,33 @@ def check_indices(idx: torch.Tensor, num_tokens: int) -> bool:
         return False
     _check("mla_check_indices", rc)
     return True
+
+
+def quantize_records(x: torch.Tensor, record_bytes: int, cache: torch.Tensor | None = None,
+                     slots: torch.Tensor | None = None) -> torch.Tensor:
+    """Quantize bf16 latents x [n, 512] into fp8 (528 B) or fp4 (288 B) records (mla_quantize_records).
+
+    With slots (int32 [n]) the records go to those token ids of `cache` (uint8 [..., record_bytes]);
+    without, row i goes to token i of `cache`, or to a new [n, record_bytes] tensor when cache is None.
+    Returns the cache tensor.
+    """
+    lib = load_library()
+    _need(x, torch.bfloat16, "x")
+    if x.dim() != 2 or x.shape[1] != HEAD_DIM:
+        raise ValueError(f"x must be [n, {HEAD_DIM}]")
+    if record_bytes not in (FP8_RECORD_BYTES, FP4_RECORD_BYTES):
+        raise ValueError("record_bytes must be 528 or 288")
+    if cache is None:
+        cache = torch.empty((x.shape[0], record_bytes), dtype=torch.uint8, device=x.device)
+    _need(cache, torch.uint8, "cache", x.device)
+    if cache.shape[-1] != record_bytes:
+        raise ValueError(f"cache records must be {record_bytes} bytes")
+    if slots is not None:
+        _need(slots, torch.int32, "slots", x.device)
+        if slots.numel() != x.shape[0]:
+            raise ValueError("one slot per row of x")
+    with torch.cuda.device(x.device):
+        _check("mla_quantize_records", lib.mla_quantize_records(
+            _ptr(x), x.shape[0], _ptr(slots), record_bytes, _ptr(cache),
+            cache.numel() // record_bytes, _stream(x.device)))
+    return cache

@@ -25,7 +25,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmla.so")
 SOURCES = ["mla_decode.hip", "mla_decode_wide.hip", "mla_sched.hip", "mla_combine.hip", "mla_aux.hip",
-           "mla_noalloc.hip", "mla_api.cpp"]
+           "mla_noalloc.hip", "mla_quant.hip", "mla_api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = [

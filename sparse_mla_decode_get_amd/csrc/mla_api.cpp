@@ -278,6 +278,22 @@ int mla_validate_indices(const int32_t* idx, int64_t n, int64_t num_tokens, int3
                                                                                        : MLA_ERR_HIP;
 }
 
+int mla_quantize_records(const void* x, int64_t n, const int32_t* slots, int record_bytes,
+                         uint8_t* cache, int64_t cache_tokens, void* stream) {
+  if (n < 0 || cache_tokens < 0) return MLA_ERR_INVALID_ARG;
+  if (record_bytes != MLA_FP8_RECORD_BYTES && record_bytes != MLA_FP4_RECORD_BYTES)
+    return MLA_ERR_UNSUPPORTED;
+  if (n == 0) return MLA_OK;
+  if (!x || !cache || !aligned(x, 16) || !aligned(cache, 16) || !aligned(slots, 4))
+    return MLA_ERR_INVALID_ARG;
+  if (!slots && n > cache_tokens) return MLA_ERR_INVALID_ARG;
+  if (n > (int64_t(1) << 33)) return MLA_ERR_UNSUPPORTED;     // grid of n / 4 workgroups
+  return mla::launch_quantize(static_cast<const uint16_t*>(x), n, slots, record_bytes, cache,
+                              cache_tokens, (hipStream_t)stream) == 0
+             ? MLA_OK
+             : MLA_ERR_HIP;
+}
+
 int mla_check_indices(const int32_t* idx, int64_t n, int64_t num_tokens, int32_t* bad_count,
                       void* stream) {
   const int rc = mla_validate_indices(idx, n, num_tokens, bad_count, stream);

@@ -76,5 +76,8 @@ int launch_dequant(const uint8_t* cache, int record_bytes, const int32_t* idx, i
                    uint16_t* out, hipStream_t stream);
 int launch_validate(const int32_t* idx, int64_t n, int64_t num_tokens, int32_t* bad,
                     hipStream_t stream);
+// Cache writer (mla_quant.hip): bf16 [n][512] -> records at token slots (row i when slots is null).
+int launch_quantize(const uint16_t* x, int64_t n, const int32_t* slots, int record_bytes,
+                    uint8_t* cache, int64_t cache_tokens, hipStream_t stream);
 
 }  // namespace mla

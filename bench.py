@@ -145,6 +145,58 @@ def bench_quantize(args):
         "cpu_baseline": None}))
 
 
+def bench_prefill(args):
+    """Sparse prefill: --seq-q query rows of one sequence (128 heads) over a 65536-token fp8 cache,
+    2048 distinct selected tokens per row with the last 0-10% ignored, values spread over 2^+-4 per
+    32-block (the headline decode's per-row recipe). Two index sets alternate between steps; the
+    selected records (~1 GB per set at 4096 rows, read with heavy reuse) come through L2/MALL."""
+    import torch
+
+    import sparse_mla_decode_get_amd as mla
+    from workloads import Spec, add_index_set, make_workload
+    mla.load_library()
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    s_q, h, topk = args.seq_q, 128, 2048
+    spec = Spec("prefill", 1, s_q, h, topk, 65536, values="spread", neg="tail10")
+    w = make_workload(spec, seed=3000)
+    sets = [w["indices"], add_index_set(w, 3001)]
+    q = torch.from_numpy(w["q_bits"].view(np.int16)).view(torch.bfloat16).to(dev).reshape(s_q, h, 512)
+    k_cache = torch.from_numpy(w["k_cache"]).to(dev)
+    idx = [torch.from_numpy(x.reshape(s_q, topk)).to(dev) for x in sets]
+    out = torch.empty((s_q, h, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((s_q, h), dtype=torch.float32, device=dev)
+
+    def step(k):
+        mla.sparse_prefill(q, k_cache, idx[k % 2], w["softmax_scale"], out=out, lse=lse)
+
+    for k in range(args.warmup):
+        step(k)
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for k in range(args.steps):
+        step(k)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    nv = np.mean([(sets[k % 2] >= 0).sum() for k in range(args.steps)])
+    flops = 2.0 * h * 1024 * nv
+    tflops = flops / (ms * 1e-3) / 1e12
+    print(json.dumps({
+        "metric": "sparse MLA prefill TFLOP/s, fp8 528B/tok, H=128 topk=2048", "value": tflops,
+        "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"sparse prefill: {s_q} query rows, h_q {h}, topk {topk} over a "
+                               "65536-token cache, 528 B fp8 records", "seq_len_q": s_q, "h_q": h,
+                   "topk": topk},
+        "roofline": {"bound": "mfma", "achieved": tflops, "peak": BF16_MFMA_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": tflops / BF16_MFMA_PEAK_TFLOPS, "traffic": None},
+        "valid_tokens_per_step": float(nv), "cpu_baseline": None}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -158,8 +210,10 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-probe", action="store_true",
                     help="run one 1 GiB device copy first (calibrates HBM byte counters)")
-    ap.add_argument("--op", choices=["decode", "quantize"], default="decode",
-                    help="decode (the hot path, default) or quantize (the cache writer)")
+    ap.add_argument("--op", choices=["decode", "quantize", "prefill"], default="decode",
+                    help="decode (the hot path, default), quantize (the cache writer) or prefill "
+                         "(sparse prefill, --seq-q query rows of one sequence)")
+    ap.add_argument("--seq-q", type=int, default=4096, help="--op prefill: query rows")
     ap.add_argument("--tokens", type=int, default=1 << 20, help="--op quantize: tokens per step")
     ap.add_argument("--record", type=int, default=528, help="--op quantize: 528 (fp8) or 288 (fp4)")
     args = ap.parse_args()
@@ -169,6 +223,9 @@ def main():
         sys.exit(2)
     if args.op == "quantize":
         bench_quantize(args)
+        return
+    if args.op == "prefill":
+        bench_prefill(args)
         return
 
     import torch

@@ -132,6 +132,23 @@ int mla_sparse_decode(const void* q, const uint8_t* k_cache, int64_t k_tokens,
                       size_t workspace_bytes, void* out, float* lse, void* stream);
 
 /*
+ * Sparse MLA prefill: the same attention for s_q query tokens of one sequence, each with its own
+ * selection (page "deepseek-ai/FlashMLA", section "How to use it", sparse prefill with a query
+ * tensor, the KV cache and an indices tensor telling each query token which KV tokens it attends
+ * to; section "What it is": the sparse kernels of both phases read the FP8/FP4 cache).
+ *   q        device bf16 [s_q][h_q][512]; out device bf16 [s_q][h_q][512]; lse device fp32 [s_q][h_q].
+ *   indices  device int32 [s_q][topk] flat token ids into k_cache (negative = ignored);
+ *            extra_k_cache / extra_indices [s_q][extra_topk] as in mla_sparse_decode.
+ * No metadata and no workspace: with many query rows, whole rows are spread evenly over the device
+ * (one part per CU and head group) and no row is split. Same checks, kernels and results per row as
+ * mla_sparse_decode with batch = 1, seq_len_q = s_q.
+ */
+int mla_sparse_prefill(const void* q, int s_q, int h_q, const uint8_t* k_cache, int64_t k_tokens,
+                       const int32_t* indices, int topk, const uint8_t* extra_k_cache,
+                       int64_t extra_tokens, const int32_t* extra_indices, int extra_topk,
+                       float softmax_scale, void* out, float* lse, void* stream);
+
+/*
  * mla_sparse_decode for callers that cannot allocate device memory: code under HIP graph capture,
  * tight serving loops, harnesses that forbid allocation. Same arguments, checks, kernels and results
  * as mla_sparse_decode, without the workspace: the split partials go to a fixed device array of

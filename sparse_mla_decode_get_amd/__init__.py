@@ -17,6 +17,7 @@ import torch
 
 __all__ = ["HEAD_DIM", "FP8_RECORD_BYTES", "FP4_RECORD_BYTES", "TILE_TOKENS", "MLAError", "Metadata",
            "library_path", "load_library", "get_metadata", "workspace_bytes", "sparse_decode",
+           "sparse_prefill",
            "combine", "dequant_records", "validate_indices", "check_indices", "quantize_records",
            "metadata_parts",
            "error_string"]
@@ -42,6 +43,8 @@ _SIG = {
                                ctypes.c_float, _VP, _VP, _I, _VP, ctypes.c_size_t, _VP, _VP, _VP]),
     "mla_sparse_decode_noalloc": (_I, [_VP, _VP, _I64, _VP, _I, _VP, _I64, _VP, _I, _I, _I, _I,
                                        ctypes.c_float, _VP, _VP, _I, _VP, _VP, _VP]),
+    "mla_sparse_prefill": (_I, [_VP, _I, _I, _VP, _I64, _VP, _I, _VP, _I64, _VP, _I, ctypes.c_float,
+                                _VP, _VP, _VP]),
     "mla_combine": (_I, [_VP, _VP, _VP, _I, _I, _VP, _VP, _VP]),
     "mla_dequant_records": (_I, [_VP, _I, _VP, _I, _VP, _VP]),
     "mla_validate_indices": (_I, [_VP, _I64, _I64, _VP, _VP]),
@@ -200,6 +203,58 @@ def sparse_decode(q: torch.Tensor, k_cache: torch.Tensor, indices: torch.Tensor,
             _ptr(extra_k_cache), x_tokens, _ptr(extra_indices), extra_topk, b, s, h,
             float(softmax_scale), _ptr(md.sched), _ptr(md.split_ptr), md.num_parts, _ptr(ws),
             0 if ws is None else ws.numel(), _ptr(out), _ptr(lse), _stream(dev)))
+    return out, lse
+
+
+def sparse_prefill(q: torch.Tensor, k_cache: torch.Tensor, indices: torch.Tensor,
+                   softmax_scale: float, extra_k_cache: torch.Tensor | None = None,
+                   extra_indices: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                   lse: torch.Tensor | None = None):
+    """out (bf16 [s_q, H, 512]), lse (fp32 [s_q, H]) = sparse MLA prefill (mla_sparse_prefill).
+
+    q: bf16 [s_q, H, 512]; k_cache uint8 [..., 528]; indices int32 [s_q, topk] (a [s_q, 1, topk]
+    tensor, one KV head, is accepted too); optional extra_k_cache [..., 288] with extra_indices
+    [s_q, extra_topk]. No metadata: rows are spread over the device whole.
+    """
+    lib = load_library()
+    _need(q, torch.bfloat16, "q")
+    dev = q.device
+    if q.dim() != 3 or q.shape[2] != HEAD_DIM:
+        raise ValueError(f"q must be [s_q, h_q, {HEAD_DIM}], got {tuple(q.shape)}")
+    s, h, _ = q.shape
+    if indices.dim() == 3 and indices.shape[1] == 1:
+        indices = indices.reshape(indices.shape[0], indices.shape[2])
+    _need(k_cache, torch.uint8, "k_cache", dev)
+    _need(indices, torch.int32, "indices", dev)
+    if k_cache.shape[-1] != FP8_RECORD_BYTES:
+        raise ValueError(f"k_cache records must be {FP8_RECORD_BYTES} bytes")
+    if indices.dim() != 2 or indices.shape[0] != s:
+        raise ValueError("indices must be [s_q, topk]")
+    extra_topk, x_tokens = 0, 0
+    if (extra_k_cache is None) != (extra_indices is None):
+        raise ValueError("extra_k_cache and extra_indices go together")
+    if extra_k_cache is not None:
+        if extra_indices.dim() == 3 and extra_indices.shape[1] == 1:
+            extra_indices = extra_indices.reshape(extra_indices.shape[0], extra_indices.shape[2])
+        _need(extra_k_cache, torch.uint8, "extra_k_cache", dev)
+        _need(extra_indices, torch.int32, "extra_indices", dev)
+        if extra_k_cache.shape[-1] != FP4_RECORD_BYTES:
+            raise ValueError(f"extra_k_cache records must be {FP4_RECORD_BYTES} bytes")
+        if extra_indices.dim() != 2 or extra_indices.shape[0] != s:
+            raise ValueError("extra_indices must be [s_q, extra_topk]")
+        extra_topk = extra_indices.shape[1]
+        x_tokens = extra_k_cache.numel() // FP4_RECORD_BYTES
+    if out is None:
+        out = torch.empty((s, h, HEAD_DIM), dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty((s, h), dtype=torch.float32, device=dev)
+    _need(out, torch.bfloat16, "out", dev)
+    _need(lse, torch.float32, "lse", dev)
+    with torch.cuda.device(dev):
+        _check("mla_sparse_prefill", lib.mla_sparse_prefill(
+            _ptr(q), s, h, _ptr(k_cache), k_cache.numel() // FP8_RECORD_BYTES, _ptr(indices),
+            indices.shape[1], _ptr(extra_k_cache), x_tokens, _ptr(extra_indices), extra_topk,
+            float(softmax_scale), _ptr(out), _ptr(lse), _stream(dev)))
     return out, lse
 
 

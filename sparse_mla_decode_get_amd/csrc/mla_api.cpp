@@ -113,8 +113,8 @@ int sparse_decode(const DecodeCall& c, const WorkspaceSource& ws) {
   if (rc != MLA_OK) return rc;
   const int rows = batch * seq_len_q;
   if (rows == 0) return MLA_OK;
-  if (!c.q || !c.out || !c.lse || !c.sched || !c.split_ptr || num_parts_used < 1)
-    return MLA_ERR_INVALID_ARG;
+  if (!c.q || !c.out || !c.lse) return MLA_ERR_INVALID_ARG;
+  if (!c.prefill && (!c.sched || !c.split_ptr || num_parts_used < 1)) return MLA_ERR_INVALID_ARG;
   if (topk > 0 && (!c.k_cache || !c.indices || c.k_tokens <= 0)) return MLA_ERR_INVALID_ARG;
   if (extra_topk > 0 && (!c.extra_k_cache || !c.extra_indices || c.extra_tokens <= 0))
     return MLA_ERR_INVALID_ARG;
@@ -127,7 +127,9 @@ int sparse_decode(const DecodeCall& c, const WorkspaceSource& ws) {
   if (num_parts_used > kMaxParts) return MLA_ERR_INVALID_ARG;
   int tiles_k = 0;
   const int tiles = tiles_per_row(topk, extra_topk, &tiles_k);
-  const bool split = any_split(rows, tiles, num_parts_used);
+  // prefill: whole rows per part, as many parts as the device runs at once (none split)
+  const int parts = c.prefill ? (rows < default_parts(h_q) ? rows : default_parts(h_q)) : num_parts_used;
+  const bool split = !c.prefill && any_split(rows, tiles, num_parts_used);
   void* part_o = nullptr;
   float* part_lse = nullptr;
   if (split) {
@@ -159,15 +161,19 @@ int sparse_decode(const DecodeCall& c, const WorkspaceSource& ws) {
   p.rows = rows;
   p.h_q = h_q;
   p.scale_log2 = c.softmax_scale * 1.4426950408889634f;
-  p.sched = c.sched;
-  p.split_ptr = c.split_ptr;
+  // prefill: the query itself stands in as the kernels' always-valid dummy load address
+  p.sched = c.prefill ? static_cast<const int32_t*>(c.q) : c.sched;
+  p.split_ptr = c.prefill ? nullptr : c.split_ptr;
+  p.prefill_parts = c.prefill ? parts : 0;
+  p.prefill_q = c.prefill ? rows / parts : 0;
+  p.prefill_r = c.prefill ? rows % parts : 0;
   p.part_o = part_o;
   p.part_lse = part_lse;
   p.out = static_cast<uint16_t*>(c.out);
   p.lse = c.lse;
   hipStream_t s = (hipStream_t)c.stream;
-  const int launched = wide_for(h_q) ? launch_sparse_decode_wide(p, num_parts_used, head_groups(h_q), s)
-                                     : launch_sparse_decode(p, num_parts_used, head_groups(h_q), 4, s);
+  const int launched = wide_for(h_q) ? launch_sparse_decode_wide(p, parts, head_groups(h_q), s)
+                                     : launch_sparse_decode(p, parts, head_groups(h_q), 4, s);
   if (launched != 0) return MLA_ERR_HIP;
   if (split) {
     const int merged = wide_for(h_q)
@@ -242,6 +248,16 @@ int mla_sparse_decode(const void* q, const uint8_t* k_cache, int64_t k_tokens,
   ws.caller_ptr = workspace;
   ws.caller_bytes = workspace_bytes;
   return mla::sparse_decode(c, ws);
+}
+
+int mla_sparse_prefill(const void* q, int s_q, int h_q, const uint8_t* k_cache, int64_t k_tokens,
+                       const int32_t* indices, int topk, const uint8_t* extra_k_cache,
+                       int64_t extra_tokens, const int32_t* extra_indices, int extra_topk,
+                       float softmax_scale, void* out, float* lse, void* stream) {
+  mla::DecodeCall c{q, k_cache, k_tokens, indices, topk, extra_k_cache, extra_tokens, extra_indices,
+                    extra_topk, 1, s_q, h_q, softmax_scale, nullptr, nullptr, 1, out, lse, stream};
+  c.prefill = true;
+  return mla::sparse_decode(c, mla::WorkspaceSource{});
 }
 
 int mla_combine(const float* partial, const float* partial_lse, const int32_t* split_ptr, int rows,

@@ -219,14 +219,25 @@ void sparse_decode_kernel(DecodeParams p) {
   float* alpha_s = reinterpret_cast<float*>(smem + C::kOffAlpha);
   int* flag_s = reinterpret_cast<int*>(smem + C::kOffFlag);
 
-  // This part's units run from (sc[0], sc[1]) to the exclusive end (sc[2], sc[3]); they are walked
+  // This part's units run from (row, t0) to the exclusive end (end_row, end_tile); they are walked
   // row segment by row segment without any division.
-  const int32_t* sc = p.sched + blockIdx.x * 8;
-  int row = sc[0];
-  int t0 = sc[1];
-  const int end_row = sc[2];
-  const int end_tile = sc[3];
-  const int slot_first = sc[4];
+  int row, t0, end_row, end_tile, slot_first;
+  if (p.prefill_parts > 0) {
+    // whole rows, evenly: part b takes prefill_q rows, plus one for the first prefill_r parts
+    const int b = (int)blockIdx.x;
+    row = b * p.prefill_q + min(b, p.prefill_r);
+    end_row = row + p.prefill_q + (b < p.prefill_r ? 1 : 0);
+    t0 = 0;
+    end_tile = 0;
+    slot_first = 0;
+  } else {
+    const int32_t* sc = p.sched + blockIdx.x * 8;
+    row = sc[0];
+    t0 = sc[1];
+    end_row = sc[2];
+    end_tile = sc[3];
+    slot_first = sc[4];
+  }
   bool first_seg = true;
 
   while (row < end_row || (row == end_row && t0 < end_tile)) {
@@ -346,8 +357,8 @@ void sparse_decode_kernel(DecodeParams p) {
     }
     // The split bookkeeping is needed only by the epilogue. It is read after the segment's first
     // copies are issued, so its memory round trip overlaps theirs instead of delaying the Q load.
-    const int split_base = p.split_ptr[row];
-    const int nsplit = p.split_ptr[row + 1] - split_base;
+    const int split_base = p.split_ptr ? p.split_ptr[row] : 0;
+    const int nsplit = p.split_ptr ? p.split_ptr[row + 1] - split_base : 1;
     const int slot = first_seg ? slot_first : split_base;
 
     // Both halves run nk iterations with the same three workgroup barriers each (a half whose

@@ -511,12 +511,23 @@ void sparse_decode_wide_kernel(DecodeParams p) {
     __syncthreads();
   }
 
-  const int32_t* sc = p.sched + blockIdx.x * 8;
-  int row = sc[0];
-  int t0 = sc[1];
-  const int end_row = sc[2];
-  const int end_tile = sc[3];
-  const int slot_first = sc[4];
+  int row, t0, end_row, end_tile, slot_first;
+  if (p.prefill_parts > 0) {
+    // whole rows, evenly: part b takes prefill_q rows, plus one for the first prefill_r parts
+    const int b = (int)blockIdx.x;
+    row = b * p.prefill_q + min(b, p.prefill_r);
+    end_row = row + p.prefill_q + (b < p.prefill_r ? 1 : 0);
+    t0 = 0;
+    end_tile = 0;
+    slot_first = 0;
+  } else {
+    const int32_t* sc = p.sched + blockIdx.x * 8;
+    row = sc[0];
+    t0 = sc[1];
+    end_row = sc[2];
+    end_tile = sc[3];
+    slot_first = sc[4];
+  }
   bool first_seg = true;
   int seg_parity = 0;
 
@@ -620,8 +631,8 @@ void sparse_decode_wide_kernel(DecodeParams p) {
       nsub = __builtin_amdgcn_readfirstlane(max(max(slots[0], slots[1]), max(slots[2], slots[3])) + 1);
       seg_parity ^= 1;
     }
-    const int split_base = p.split_ptr[row];
-    const int nsplit = p.split_ptr[row + 1] - split_base;
+    const int split_base = p.split_ptr ? p.split_ptr[row] : 0;
+    const int nsplit = p.split_ptr ? p.split_ptr[row + 1] - split_base : 1;
     const int slot = first_seg ? slot_first : split_base;
 
     // Q and the first two index rows are resident before any further asynchronous copy of this

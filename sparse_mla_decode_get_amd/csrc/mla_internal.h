@@ -16,8 +16,10 @@ struct DecodeParams {
   int tiles_k, tiles;        // fp8 units per row, all units per row
   int rows, h_q;
   float scale_log2;          // softmax_scale * log2(e)
-  const int32_t* sched;      // [parts][8]
-  const int32_t* split_ptr;  // [rows + 1]
+  const int32_t* sched;      // [parts][8]; with prefill_parts > 0 only a valid dummy address
+  const int32_t* split_ptr;  // [rows + 1]; null with prefill_parts > 0 (no row is split)
+  int prefill_parts;         // > 0: no metadata; part b takes whole rows, prefill_q of them plus
+  int prefill_q, prefill_r;  // one for b < prefill_r (rows = prefill_q * parts + prefill_r)
   void* part_o;              // workspace partial outputs [slots][h_q][512]: fp32 from the 128-head
                              // kernel, bf16 from the 64-head kernel
   float* part_lse;           // workspace partial lse [slots][h_q]
@@ -44,6 +46,7 @@ struct DecodeCall {
   void* out;
   float* lse;
   void* stream;
+  bool prefill = false;      // mla_sparse_prefill: no metadata, whole rows per part, no split
 };
 
 // Where the split partials go: the caller's workspace (mla_sparse_decode), or, when fixed_bytes > 0,

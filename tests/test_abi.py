@@ -156,3 +156,17 @@ def test_shapes_whose_partition_could_overflow_are_refused(lib):
 def test_check_indices_argument_errors(lib):
     assert lib.mla_check_indices(None, 4, 10, None, None) == -1
     assert lib.mla_check_indices(None, -1, 10, 1 << 20, None) == -1
+
+
+def test_prefill_argument_errors(lib):
+    null = None
+    # null q / cache / indices -> invalid argument; zero rows -> no-op; bad scale -> invalid
+    assert lib.mla_sparse_prefill(null, 4, 64, null, 0, null, 16, null, 0, null, 0, 0.04, null, null,
+                                  null) == -1
+    assert lib.mla_sparse_prefill(null, 0, 64, null, 0, null, 16, null, 0, null, 0, 0.04, null, null,
+                                  null) == 0
+    a = 1 << 20
+    assert lib.mla_sparse_prefill(a, 4, 64, 2 * a, 100, 3 * a, 16, null, 0, null, 0, -1.0, 4 * a,
+                                  5 * a, null) == -1
+    assert lib.mla_sparse_prefill(a + 2, 4, 64, 2 * a, 100, 3 * a, 16, null, 0, null, 0, 0.04,
+                                  4 * a, 5 * a, null) == -1

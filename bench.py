@@ -210,9 +210,10 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-probe", action="store_true",
                     help="run one 1 GiB device copy first (calibrates HBM byte counters)")
-    ap.add_argument("--op", choices=["decode", "quantize", "prefill"], default="decode",
-                    help="decode (the hot path, default), quantize (the cache writer) or prefill "
-                         "(sparse prefill, --seq-q query rows of one sequence)")
+    ap.add_argument("--op", choices=["decode", "quantize", "prefill", "fused"], default="decode",
+                    help="decode (the hot path, default), quantize (the cache writer), prefill "
+                         "(sparse prefill, --seq-q query rows of one sequence) or fused (the fused "
+                         "norm-RoPE-attention-RoPE-fp8 decode on the --config workload)")
     ap.add_argument("--seq-q", type=int, default=4096, help="--op prefill: query rows")
     ap.add_argument("--tokens", type=int, default=1 << 20, help="--op quantize: tokens per step")
     ap.add_argument("--record", type=int, default=528, help="--op quantize: 528 (fp8) or 288 (fp4)")
@@ -279,10 +280,25 @@ def main():
     torch.cuda.synchronize()
     metadata_ms = e0.elapsed_time(e1)
 
+    if args.op == "fused":
+        # the fused decode reads the raw query: an RMSNorm weight near 1 and rotary angles of
+        # random positions (base 10000 over the 32 pairs), as a model's decode step would pass
+        rng = np.random.default_rng(9)
+        qn_w = torch.from_numpy((1 + 0.1 * rng.standard_normal(512)).astype(np.float32)).to(
+            torch.bfloat16).to(dev)
+        ang = rng.integers(0, 65536, b * s)[:, None] * 10000.0 ** (-np.arange(32) / 32.0)
+        r_cos = torch.from_numpy(np.cos(ang).astype(np.float32).reshape(b, s, 32)).to(dev)
+        r_sin = torch.from_numpy(np.sin(ang).astype(np.float32).reshape(b, s, 32)).to(dev)
+        out = torch.empty((b, s, h, 528), dtype=torch.uint8, device=dev)
+
     def step(k):
         j = k % len(idx_sets)
-        mla.sparse_decode(q, k_cache, idx_sets[j], w["softmax_scale"], md, xc, xidx_sets[j],
-                          out=out, lse=lse)
+        if args.op == "fused":
+            mla.sparse_decode_fused(q, qn_w, 1e-6, r_cos, r_sin, k_cache, idx_sets[j],
+                                    w["softmax_scale"], md, xc, xidx_sets[j], out=out, lse=lse)
+        else:
+            mla.sparse_decode(q, k_cache, idx_sets[j], w["softmax_scale"], md, xc, xidx_sets[j],
+                              out=out, lse=lse)
 
     for k in range(args.warmup):
         step(k)
@@ -348,7 +364,8 @@ def main():
         cpu = cpu_baseline(w, args.cpu_seconds)
 
     line = {
-        "metric": METRIC,
+        "metric": METRIC if args.op == "decode" else
+        "fused norm-RoPE-sparse MLA-RoPE-fp8 decode TFLOP/s, fp8 528B/tok, B=128 H=128 topk=2048",
         "value": tflops,
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -360,7 +377,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"{spec.name} sparse MLA decode: batch {b}, seq_len_q {s}, h_q {h}, "
+        "config": {"workload": f"{spec.name} {'fused ' if args.op == 'fused' else ''}sparse MLA decode: batch {b}, seq_len_q {s}, h_q {h}, "
                                f"topk {spec.topk}" + (f" + extra {spec.extra_topk} fp4" if spec.extra_topk else "")
                                + f", {spec.tokens_per_seq} tokens per sequence in 64-token blocks, "
                                f"528 B fp8 records",

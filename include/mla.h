@@ -132,6 +132,36 @@ int mla_sparse_decode(const void* q, const uint8_t* k_cache, int64_t k_tokens,
                       size_t workspace_bytes, void* out, float* lse, void* stream);
 
 /*
+ * Fused decode: Q-norm, RoPE, the sparse attention, conjugate RoPE on the output and the cast to
+ * FP8, in one launch (page "deepseek-ai/FlashMLA", section "What it is": the fused kernel; section
+ * "How to use it": the decode call returns FP8 outputs for a downstream FP8 einsum). Supported for
+ * h_q > 64 (the 128-head kernel); MLA_ERR_UNSUPPORTED otherwise. The pages leave the details open;
+ * this library's reading:
+ *   q              device bf16 [batch][seq_len_q][h_q][512], the query BEFORE normalisation.
+ *   q_norm_weight  device bf16 [512], 16-byte aligned: each head row becomes
+ *                  q / sqrt(mean(q^2) + q_norm_eps) * q_norm_weight (RMSNorm over the 512 dims).
+ *   rope_cos, rope_sin  device fp32 [batch][seq_len_q][32], 16-byte aligned: the rotary part is the
+ *                  last 64 latent dims as 32 interleaved pairs (448 + 2i, 449 + 2i); pair i of row r
+ *                  is rotated by the angle with cosine rope_cos[r][i] and sine rope_sin[r][i]:
+ *                  (x0, x1) -> (x0 c - x1 s, x0 s + x1 c). The rotated query enters QK^T as bf16.
+ *   out_fp8        device uint8 [batch][seq_len_q][h_q][528], 16-byte aligned: each output row,
+ *                  with its rotary pairs rotated back ((y0, y1) -> (y0 c + y1 s, y1 c - y0 s)),
+ *                  stored as an fp8 record in the cache's own format (512 e4m3 values, then 16 e8m0
+ *                  scales, one per 32 values; scale 2^ceil(log2(amax / 448)), values rounded to
+ *                  nearest, ties to even). A row with no valid entry stores zeros with scale bytes 127.
+ *   lse            as in mla_sparse_decode (of the scores of the normalised, rotated query).
+ * All other arguments, the metadata and the workspace are those of mla_sparse_decode.
+ */
+int mla_sparse_decode_fused(const void* q, const void* q_norm_weight, float q_norm_eps,
+                            const float* rope_cos, const float* rope_sin, const uint8_t* k_cache,
+                            int64_t k_tokens, const int32_t* indices, int topk,
+                            const uint8_t* extra_k_cache, int64_t extra_tokens,
+                            const int32_t* extra_indices, int extra_topk, int batch, int seq_len_q,
+                            int h_q, float softmax_scale, const int32_t* sched,
+                            const int32_t* split_ptr, int num_parts_used, void* workspace,
+                            size_t workspace_bytes, uint8_t* out_fp8, float* lse, void* stream);
+
+/*
  * Sparse MLA prefill: the same attention for s_q query tokens of one sequence, each with its own
  * selection (page "deepseek-ai/FlashMLA", section "How to use it", sparse prefill with a query
  * tensor, the KV cache and an indices tensor telling each query token which KV tokens it attends

@@ -17,7 +17,7 @@ import torch
 
 __all__ = ["HEAD_DIM", "FP8_RECORD_BYTES", "FP4_RECORD_BYTES", "TILE_TOKENS", "MLAError", "Metadata",
            "library_path", "load_library", "get_metadata", "workspace_bytes", "sparse_decode",
-           "sparse_prefill",
+           "sparse_prefill", "sparse_decode_fused",
            "combine", "dequant_records", "validate_indices", "check_indices", "quantize_records",
            "metadata_parts",
            "error_string"]
@@ -43,6 +43,9 @@ _SIG = {
                                ctypes.c_float, _VP, _VP, _I, _VP, ctypes.c_size_t, _VP, _VP, _VP]),
     "mla_sparse_decode_noalloc": (_I, [_VP, _VP, _I64, _VP, _I, _VP, _I64, _VP, _I, _I, _I, _I,
                                        ctypes.c_float, _VP, _VP, _I, _VP, _VP, _VP]),
+    "mla_sparse_decode_fused": (_I, [_VP, _VP, ctypes.c_float, _VP, _VP, _VP, _I64, _VP, _I, _VP, _I64,
+                                     _VP, _I, _I, _I, _I, ctypes.c_float, _VP, _VP, _I, _VP,
+                                     ctypes.c_size_t, _VP, _VP, _VP]),
     "mla_sparse_prefill": (_I, [_VP, _I, _I, _VP, _I64, _VP, _I, _VP, _I64, _VP, _I, ctypes.c_float,
                                 _VP, _VP, _VP]),
     "mla_combine": (_I, [_VP, _VP, _VP, _I, _I, _VP, _VP, _VP]),
@@ -200,6 +203,60 @@ def sparse_decode(q: torch.Tensor, k_cache: torch.Tensor, indices: torch.Tensor,
     with torch.cuda.device(dev):
         _check("mla_sparse_decode", lib.mla_sparse_decode(
             _ptr(q), _ptr(k_cache), k_cache.numel() // FP8_RECORD_BYTES, _ptr(indices), topk,
+            _ptr(extra_k_cache), x_tokens, _ptr(extra_indices), extra_topk, b, s, h,
+            float(softmax_scale), _ptr(md.sched), _ptr(md.split_ptr), md.num_parts, _ptr(ws),
+            0 if ws is None else ws.numel(), _ptr(out), _ptr(lse), _stream(dev)))
+    return out, lse
+
+
+def sparse_decode_fused(q: torch.Tensor, q_norm_weight: torch.Tensor, q_norm_eps: float,
+                        rope_cos: torch.Tensor, rope_sin: torch.Tensor, k_cache: torch.Tensor,
+                        indices: torch.Tensor, softmax_scale: float, metadata: Metadata,
+                        extra_k_cache: torch.Tensor | None = None,
+                        extra_indices: torch.Tensor | None = None,
+                        out: torch.Tensor | None = None, lse: torch.Tensor | None = None):
+    """out_fp8 (uint8 [B, S, H, 528] records), lse (fp32 [B, S, H]) = the fused decode
+    (mla_sparse_decode_fused): RMSNorm (weight bf16 [512]) and RoPE (cos/sin fp32 [B, S, 32]) of the
+    raw query q (bf16 [B, S, H, 512]), sparse attention, conjugate RoPE and the fp8 cast."""
+    lib = load_library()
+    _need(q, torch.bfloat16, "q")
+    dev = q.device
+    if q.dim() != 4 or q.shape[3] != HEAD_DIM:
+        raise ValueError(f"q must be [batch, seq_len_q, h_q, {HEAD_DIM}]")
+    b, s, h, _ = q.shape
+    _need(q_norm_weight, torch.bfloat16, "q_norm_weight", dev)
+    _need(rope_cos, torch.float32, "rope_cos", dev)
+    _need(rope_sin, torch.float32, "rope_sin", dev)
+    if q_norm_weight.numel() != HEAD_DIM or tuple(rope_cos.shape) != (b, s, 32) or \
+            tuple(rope_sin.shape) != (b, s, 32):
+        raise ValueError("q_norm_weight must hold 512 values, rope_cos / rope_sin [batch, seq_len_q, 32]")
+    _need(k_cache, torch.uint8, "k_cache", dev)
+    _need(indices, torch.int32, "indices", dev)
+    if indices.dim() != 3 or tuple(indices.shape[:2]) != (b, s):
+        raise ValueError("indices must be [batch, seq_len_q, topk]")
+    topk = indices.shape[2]
+    extra_topk, x_tokens = 0, 0
+    if (extra_k_cache is None) != (extra_indices is None):
+        raise ValueError("extra_k_cache and extra_indices go together")
+    if extra_k_cache is not None:
+        _need(extra_k_cache, torch.uint8, "extra_k_cache", dev)
+        _need(extra_indices, torch.int32, "extra_indices", dev)
+        extra_topk = extra_indices.shape[2]
+        x_tokens = extra_k_cache.numel() // FP4_RECORD_BYTES
+    md = metadata
+    if (md.batch, md.seq_len_q, md.h_q, md.topk, md.extra_topk) != (b, s, h, topk, extra_topk):
+        raise ValueError("metadata was computed for a different shape")
+    if out is None:
+        out = torch.empty((b, s, h, FP8_RECORD_BYTES), dtype=torch.uint8, device=dev)
+    if lse is None:
+        lse = torch.empty((b, s, h), dtype=torch.float32, device=dev)
+    _need(out, torch.uint8, "out", dev)
+    _need(lse, torch.float32, "lse", dev)
+    ws = md.workspace
+    with torch.cuda.device(dev):
+        _check("mla_sparse_decode_fused", lib.mla_sparse_decode_fused(
+            _ptr(q), _ptr(q_norm_weight), float(q_norm_eps), _ptr(rope_cos), _ptr(rope_sin),
+            _ptr(k_cache), k_cache.numel() // FP8_RECORD_BYTES, _ptr(indices), topk,
             _ptr(extra_k_cache), x_tokens, _ptr(extra_indices), extra_topk, b, s, h,
             float(softmax_scale), _ptr(md.sched), _ptr(md.split_ptr), md.num_parts, _ptr(ws),
             0 if ws is None else ws.numel(), _ptr(out), _ptr(lse), _stream(dev)))

@@ -114,6 +114,14 @@ int sparse_decode(const DecodeCall& c, const WorkspaceSource& ws) {
   const int rows = batch * seq_len_q;
   if (rows == 0) return MLA_OK;
   if (!c.q || !c.out || !c.lse) return MLA_ERR_INVALID_ARG;
+  if (c.fused) {
+    // the fused query transform and fp8 output live in the 128-head kernel only
+    if (!wide_for(h_q)) return MLA_ERR_UNSUPPORTED;
+    if (!c.qn_weight || !c.rope_cos || !c.rope_sin || !aligned(c.qn_weight, 16) ||
+        !aligned(c.rope_cos, 16) || !aligned(c.rope_sin, 16) || !aligned(c.out, 16) ||
+        !std::isfinite(c.qn_eps) || c.qn_eps < 0.0f || c.prefill)
+      return MLA_ERR_INVALID_ARG;
+  }
   if (!c.prefill && (!c.sched || !c.split_ptr || num_parts_used < 1)) return MLA_ERR_INVALID_ARG;
   if (topk > 0 && (!c.k_cache || !c.indices || c.k_tokens <= 0)) return MLA_ERR_INVALID_ARG;
   if (extra_topk > 0 && (!c.extra_k_cache || !c.extra_indices || c.extra_tokens <= 0))
@@ -169,13 +177,22 @@ int sparse_decode(const DecodeCall& c, const WorkspaceSource& ws) {
   p.prefill_r = c.prefill ? rows % parts : 0;
   p.part_o = part_o;
   p.part_lse = part_lse;
-  p.out = static_cast<uint16_t*>(c.out);
+  p.out = c.fused ? nullptr : static_cast<uint16_t*>(c.out);
   p.lse = c.lse;
+  p.qn_weight = static_cast<const uint16_t*>(c.qn_weight);
+  p.qn_eps = c.qn_eps;
+  p.rope_cos = c.rope_cos;
+  p.rope_sin = c.rope_sin;
+  p.out_fp8 = c.fused ? static_cast<uint8_t*>(c.out) : nullptr;
   hipStream_t s = (hipStream_t)c.stream;
   const int launched = wide_for(h_q) ? launch_sparse_decode_wide(p, parts, head_groups(h_q), s)
                                      : launch_sparse_decode(p, parts, head_groups(h_q), 4, s);
   if (launched != 0) return MLA_ERR_HIP;
-  if (split) {
+  if (split && c.fused) {
+    if (launch_combine_fused(static_cast<const float*>(part_o), part_lse, c.split_ptr, rows, h_q,
+                             c.rope_cos, c.rope_sin, p.out_fp8, c.lse, s) != 0)
+      return MLA_ERR_HIP;
+  } else if (split) {
     const int merged = wide_for(h_q)
         ? launch_combine(static_cast<const float*>(part_o), part_lse, c.split_ptr, rows, h_q, p.out,
                          c.lse, true, s)
@@ -244,6 +261,28 @@ int mla_sparse_decode(const void* q, const uint8_t* k_cache, int64_t k_tokens,
   const mla::DecodeCall c{q, k_cache, k_tokens, indices, topk, extra_k_cache, extra_tokens,
                           extra_indices, extra_topk, batch, seq_len_q, h_q, softmax_scale, sched,
                           split_ptr, num_parts_used, out, lse, stream};
+  mla::WorkspaceSource ws;
+  ws.caller_ptr = workspace;
+  ws.caller_bytes = workspace_bytes;
+  return mla::sparse_decode(c, ws);
+}
+
+int mla_sparse_decode_fused(const void* q, const void* q_norm_weight, float q_norm_eps,
+                            const float* rope_cos, const float* rope_sin, const uint8_t* k_cache,
+                            int64_t k_tokens, const int32_t* indices, int topk,
+                            const uint8_t* extra_k_cache, int64_t extra_tokens,
+                            const int32_t* extra_indices, int extra_topk, int batch, int seq_len_q,
+                            int h_q, float softmax_scale, const int32_t* sched,
+                            const int32_t* split_ptr, int num_parts_used, void* workspace,
+                            size_t workspace_bytes, uint8_t* out_fp8, float* lse, void* stream) {
+  mla::DecodeCall c{q, k_cache, k_tokens, indices, topk, extra_k_cache, extra_tokens, extra_indices,
+                    extra_topk, batch, seq_len_q, h_q, softmax_scale, sched, split_ptr,
+                    num_parts_used, out_fp8, lse, stream};
+  c.fused = true;
+  c.qn_weight = q_norm_weight;
+  c.qn_eps = q_norm_eps;
+  c.rope_cos = rope_cos;
+  c.rope_sin = rope_sin;
   mla::WorkspaceSource ws;
   ws.caller_ptr = workspace;
   ws.caller_bytes = workspace_bytes;

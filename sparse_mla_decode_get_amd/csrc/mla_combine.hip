@@ -79,6 +79,76 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
   if (threadIdx.x == 0) lse[(int64_t)row * h_q + head] = wsum > 0.0f ? m + __logf(wsum) : ninf;
 }
 
+// The same merge for the fused decode's split rows: the merged row's rotary pairs (dims 448 + 2i,
+// 449 + 2i) are rotated back by the row's angle and the row is stored as an fp8 record (512 e4m3
+// values, then 16 e8m0 scales; a 32-dim block is the 8 threads 8b .. 8b+7 of one wave).
+__global__ __launch_bounds__(kCombineThreads) void combine_fused_kernel(
+    const float* __restrict__ partial, const float* __restrict__ partial_lse,
+    const int32_t* __restrict__ split_ptr, int h_q, const float* __restrict__ rope_cos,
+    const float* __restrict__ rope_sin, uint8_t* __restrict__ out_fp8, float* __restrict__ lse) {
+  const int row = blockIdx.x;
+  const int head = blockIdx.y;
+  const int a = split_ptr[row];
+  const int n = split_ptr[row + 1] - a;
+  if (n == 1) return;                      // written directly by the decode kernel
+  const float ninf = -__builtin_inff();
+  const int t = threadIdx.x;
+  const int dim = 4 * t;
+  const float* lse_col = partial_lse + (int64_t)a * h_q + head;
+  const float* o_col = partial + ((int64_t)a * h_q + head) * kHeadDim + dim;
+  float m = ninf, wsum = 0.0f;
+  f32x4 acc = f32x4{};
+  for (int i = 0; i < n; ++i) {            // two passes are not needed: rescale as the max grows
+    const float li = lse_col[(int64_t)i * h_q];
+    if (li == ninf) continue;
+    const f32x4 o = load4(o_col + (int64_t)i * h_q * kHeadDim);
+    const float mn = fmaxf(m, li);
+    const float sc = __expf(m - mn);
+    const float w = __expf(li - mn);
+    acc = acc * sc + w * o;
+    wsum = wsum * sc + w;
+    m = mn;
+  }
+  const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
+  float y[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) y[i] = acc[i] * inv;
+  if (dim >= 448) {
+    const int pi = (dim - 448) / 2;         // pairs pi and pi + 1
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      const float c = rope_cos[(int64_t)row * 32 + pi + jj], sn = rope_sin[(int64_t)row * 32 + pi + jj];
+      const float x0 = y[2 * jj], x1 = y[2 * jj + 1];
+      y[2 * jj] = x0 * c + x1 * sn;
+      y[2 * jj + 1] = x1 * c - x0 * sn;
+    }
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) amax = fmaxf(amax, __builtin_fabsf(y[i]));
+  const int lane = t & 63;
+#pragma unroll
+  for (int msk = 1; msk < 8; msk <<= 1)
+    amax = fmaxf(amax, __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(
+                           (lane ^ msk) << 2, __builtin_bit_cast(int, amax))));
+  const int k = fp8_block_exponent(amax);
+  uint32_t w = 0u;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) w |= e4m3_code(__builtin_ldexpf(y[i], -k)) << (8 * i);
+  uint8_t* rec = out_fp8 + ((int64_t)row * h_q + head) * kFp8Rec;
+  *reinterpret_cast<uint32_t*>(rec + dim) = w;
+  if ((t & 7) == 0) rec[kHeadDim + (t >> 3)] = (uint8_t)(k + 127);
+  if (t == 0) lse[(int64_t)row * h_q + head] = wsum > 0.0f ? m + __logf(wsum) : ninf;
+}
+
+int launch_combine_fused(const float* partial, const float* partial_lse, const int32_t* split_ptr,
+                         int rows, int h_q, const float* rope_cos, const float* rope_sin,
+                         uint8_t* out_fp8, float* lse, hipStream_t stream) {
+  hipLaunchKernelGGL(combine_fused_kernel, dim3(rows, h_q), dim3(kCombineThreads), 0, stream, partial,
+                     partial_lse, split_ptr, h_q, rope_cos, rope_sin, out_fp8, lse);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
 int launch_combine(const float* partial, const float* partial_lse, const int32_t* split_ptr,
                    int rows, int h_q, uint16_t* out, float* lse, bool skip_single,
                    hipStream_t stream) {

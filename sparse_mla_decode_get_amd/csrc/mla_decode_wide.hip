@@ -69,6 +69,8 @@ constexpr int kIdxBytes = kSubTokens * 4;     // one index slot (lanes 0..31 wri
 // epilogue staging of the bf16 output: 32 rows of 1 KB per wave, from the start of LDS
 constexpr int kStageRow = 1024;
 constexpr int kStageBytes = 32 * kStageRow;
+constexpr int kFusedRow = kFp8Rec;            // fused decode: one fp8 record per staged head row
+static_assert(32 * kFusedRow <= kStageBytes, "the fp8 records fit the bf16 staging");
 constexpr int kStages = 3;
 constexpr int kOffRaw = kStages * kTileBytes;
 constexpr int kOffIdx = kOffRaw + kStages * kRawBytes;
@@ -486,7 +488,7 @@ __device__ __forceinline__ void pv_chain(const uint32_t (&a)[8], f32x16 (&o)[16]
       : "memory", "v232", "v233", "v234", "v235", "v236", "v237", "v238", "v239", "v240", "v241", "v242", "v243", "v244", "v245", "v246", "v247", "v248", "v249", "v250", "v251", "v252", "v253", "v254", "v255");
 }
 
-template <bool EXTRA>
+template <bool EXTRA, bool FUSED>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void sparse_decode_wide_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
@@ -556,7 +558,7 @@ void sparse_decode_wide_kernel(DecodeParams p) {
     // the pipeline and Q are all issued before anything waits, so their latencies overlap.
     // opaque, so that nothing derived from the thread index is hoisted out of the segment loop
     // and kept live through the pipeline
-    int tid = (int)threadIdx.x;
+    int tid = 64 * wave + lane_id();       // threadIdx.x, rebuilt so that v0 need not stay live
     asm volatile("" : "+v"(tid));
     // Entry e of the segment is entry e % 32 of its sub-tile e / 32. The 8 loads of a batch are
     // unconditional (clamped addresses; an empty selection reads the schedule instead), so they
@@ -595,6 +597,66 @@ void sparse_decode_wide_kernel(DecodeParams p) {
           p.q + ((int64_t)row * p.h_q + qh) * kHeadDim + 8 * (lane >> 5));
 #pragma unroll
       for (int kk = 0; kk < 32; ++kk) qreg[kk] = __builtin_bit_cast(bf16x8, qp[2 * kk]);
+    }
+    if constexpr (FUSED) {
+      // Fused decode: the query row is RMS-normalised with the weight w (q / sqrt(mean(q^2) + eps)
+      // * w) and its rotary pairs (dims 448 + 2i, 449 + 2i; k-steps 28..31) are rotated by the row's
+      // cos / sin, in fp32, then rounded back to bf16 (page "deepseek-ai/FlashMLA", section "What
+      // it is": Q-norm and RoPE in the same kernel as the attention). Lanes l and l ^ 32 hold the
+      // two halves of head l % 32's dims.
+      const int lane = lane_id();
+      const int g = lane >> 5;
+      // the sum of squares in fp64 (each bf16 square is exact there, and 512 terms lose almost
+      // nothing), so that the roundings before the bf16 query are those of the mean, the
+      // reciprocal square root and the fp32 products below, each of order 2^-24
+      double ss = 0.0;
+#pragma unroll
+      for (int kk = 0; kk < 32; ++kk)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const double v = (double)(float)qreg[kk][j];
+          ss = __builtin_fma(v, v, ss);
+        }
+      {
+        // lanes l and l ^ 32: each swap returns this lane's word and the partner's, in an order
+        // that depends on the lane half, so both are rebuilt and added (the sum is symmetric)
+        const uint64_t b = __builtin_bit_cast(uint64_t, ss);
+        const auto lo = __builtin_amdgcn_permlane32_swap((uint32_t)b, (uint32_t)b, false, false);
+        const auto hi = __builtin_amdgcn_permlane32_swap((uint32_t)(b >> 32), (uint32_t)(b >> 32), false, false);
+        ss = __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi[0] << 32) | (uint32_t)lo[0]) +
+             __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi[1] << 32) | (uint32_t)lo[1]);
+      }
+      // opaque: the products below convert qreg again instead of keeping 256 converted values live
+#pragma unroll
+      for (int kk = 0; kk < 32; ++kk) asm volatile("" : "+v"(qreg[kk]));
+      float eps = p.qn_eps;
+      asm volatile("" : "+s"(eps));    // converted here, not kept live across the whole kernel
+      const float inv_rms = 1.0f / __builtin_sqrtf((float)(ss * (1.0 / kHeadDim) + (double)eps));
+      const u32x4* wp = reinterpret_cast<const u32x4*>(p.qn_weight + 8 * g);
+      const float* cs = p.rope_cos + (int64_t)row * 32 + 4 * g;
+      const float* sn = p.rope_sin + (int64_t)row * 32 + 4 * g;
+#pragma unroll
+      for (int kk = 0; kk < 32; ++kk) {
+        const bf16x8 wv = __builtin_bit_cast(bf16x8, wp[2 * kk]);
+        float y[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) y[j] = (float)qreg[kk][j] * inv_rms * (float)wv[j];
+        if (kk >= 28) {
+          // dims 16 kk + 8 g + j: pair 8 (kk - 28) + 4 g + j / 2
+          const f32x4 c = *reinterpret_cast<const f32x4*>(cs + 8 * (kk - 28));
+          const f32x4 sv = *reinterpret_cast<const f32x4*>(sn + 8 * (kk - 28));
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const float x0 = y[2 * jj], x1 = y[2 * jj + 1];
+            y[2 * jj] = x0 * c[jj] - x1 * sv[jj];
+            y[2 * jj + 1] = x0 * sv[jj] + x1 * c[jj];
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) qreg[kk][j] = (__bf16)y[j];
+        // one k-step at a time: the weight and angle loads are not hoisted into registers
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
 
     // ---- live length of the segment. A sub-tile whose 32 entries are all ignored (negative, or
@@ -1228,7 +1290,67 @@ void sparse_decode_wide_kernel(DecodeParams p) {
       const int head = head_base + h;
       const bool final_out = nsplit == 1;
       const float inv = l_sum > 0.0f ? 1.0f / l_sum : 0.0f;
-      if (final_out) {
+      if (FUSED && final_out) {
+        // Fused decode: the rotary pairs of the output (blocks 14 and 15: dims 448 + 2i, 449 + 2i)
+        // are rotated back by the row's angle and every head row is cast to an fp8 record (512
+        // e4m3 values, then 16 e8m0 scales, one per 32-dim block d: k = ceil(log2(amax / 448)),
+        // values rounded to nearest, ties to even), staged in LDS (kFusedRow bytes per head) and
+        // stored as whole 528-byte records.
+        char* const stage = smem + wave * kStageBytes;
+        const float* cs = p.rope_cos + (int64_t)row * 32 + 2 * g;
+        const float* sn = p.rope_sin + (int64_t)row * 32 + 2 * g;
+        uint32_t kb[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int d = 0; d < 16; ++d) {
+          float y[16];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) y[r] = oacc[d][r] * inv;
+          if (d >= 14) {
+            // dims 32 d + 8 rb + 4 g + {0..3}: pairs 16 (d - 14) + 4 rb + 2 g + {0, 1}
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb) {
+              const f32x2 c = *reinterpret_cast<const f32x2*>(cs + 16 * (d - 14) + 4 * rb);
+              const f32x2 sv = *reinterpret_cast<const f32x2*>(sn + 16 * (d - 14) + 4 * rb);
+#pragma unroll
+              for (int jj = 0; jj < 2; ++jj) {
+                const float x0 = y[4 * rb + 2 * jj], x1 = y[4 * rb + 2 * jj + 1];
+                y[4 * rb + 2 * jj] = x0 * c[jj] + x1 * sv[jj];
+                y[4 * rb + 2 * jj + 1] = x1 * c[jj] - x0 * sv[jj];
+              }
+            }
+          }
+          float a = 0.0f;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) a = fmaxf(a, __builtin_fabsf(y[r]));
+          a = max_xor32(a);
+          const int k = fp8_block_exponent(a);
+#pragma unroll
+          for (int rb = 0; rb < 4; ++rb) {
+            uint32_t w = 0u;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) w |= e4m3_code(__builtin_ldexpf(y[4 * rb + i], -k)) << (8 * i);
+            *reinterpret_cast<__attribute__((address_space(3))) uint32_t*>(
+                lds_addr(stage + h * kFusedRow + 32 * d + 8 * rb + 4 * g)) = w;
+          }
+          kb[d >> 2] |= (uint32_t)(k + 127) << (8 * (d & 3));
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if (g == 0) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            *reinterpret_cast<__attribute__((address_space(3))) uint32_t*>(
+                lds_addr(stage + h * kFusedRow + kHeadDim + 4 * i)) = kb[i];
+        }
+        // record rr, 16-byte chunk c (33 per record) from lane (33 rr + c) % 64
+        for (int e = lane; e < 32 * (kFusedRow / 16); e += 64) {
+          const int rr = e / (kFusedRow / 16), c = e % (kFusedRow / 16);
+          if (head_base + rr < p.h_q) {
+            const u32x4 v = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+                lds_addr(stage + rr * kFusedRow + 16 * c));
+            *reinterpret_cast<u32x4*>(p.out_fp8 + ((int64_t)row * p.h_q + head_base + rr) * kFp8Rec + 16 * c) = v;
+          }
+        }
+      } else if (final_out) {
         // Final rows in bf16, staged through LDS so that every store writes one head's 1 KB row:
         // the wave's 32 rows go to its own 32 KB (the tiles and the start of the raw slots, free
         // after the pass), 8-byte unit u of row h at unit u ^ h (free of bank conflicts both
@@ -1286,10 +1408,18 @@ void sparse_decode_wide_kernel(DecodeParams p) {
 
 int launch_sparse_decode_wide(const DecodeParams& p, int parts, int groups, hipStream_t stream) {
   dim3 grid(parts, groups);
-  if (p.extra_topk > 0)
-    hipLaunchKernelGGL(sparse_decode_wide_kernel<true>, grid, dim3(64 * kWaves), 0, stream, p);
-  else
-    hipLaunchKernelGGL(sparse_decode_wide_kernel<false>, grid, dim3(64 * kWaves), 0, stream, p);
+  const bool fused = p.out_fp8 != nullptr;
+  if (p.extra_topk > 0) {
+    if (fused)
+      hipLaunchKernelGGL((sparse_decode_wide_kernel<true, true>), grid, dim3(64 * kWaves), 0, stream, p);
+    else
+      hipLaunchKernelGGL((sparse_decode_wide_kernel<true, false>), grid, dim3(64 * kWaves), 0, stream, p);
+  } else {
+    if (fused)
+      hipLaunchKernelGGL((sparse_decode_wide_kernel<false, true>), grid, dim3(64 * kWaves), 0, stream, p);
+    else
+      hipLaunchKernelGGL((sparse_decode_wide_kernel<false, false>), grid, dim3(64 * kWaves), 0, stream, p);
+  }
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

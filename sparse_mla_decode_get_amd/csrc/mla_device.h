@@ -78,6 +78,37 @@ __device__ __forceinline__ void dequant_fp4_16(uint32_t w0, uint32_t w1, float s
             fp4_byte<3>(w1, scale));
 }
 
+// Nearest e4m3 code of a finite f32 (ties to even), saturating at +-448, sign kept.
+__device__ __forceinline__ uint32_t e4m3_code(float y) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, y);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7FFFFFFFu;
+  uint32_t code;
+  if (a < 0x3C800000u) {
+    // below 2^-6, the subnormal grid m * 2^-9 (m = 8 is the smallest normal, code 0x08)
+    code = (uint32_t)__builtin_rintf(__builtin_bit_cast(float, a) * 512.0f);
+  } else {
+    // drop 20 of the 23 mantissa bits, rounding to nearest with ties to even (a carry moves into
+    // the exponent field), then rebias the exponent from 127 to 7
+    const uint32_t r = (a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20;
+    code = r - (120u << 3);
+    code = code > 0x7Eu ? 0x7Eu : code;
+  }
+  return sign | code;
+}
+
+// k = ceil(log2(a / 448)) for a finite a >= 0, clipped to [-127, 127]; 0 for a = 0. With
+// a = M * 2^E, M in [1, 2): k = E - 8 if M <= 1.75, else E - 7 (448 = 1.75 * 2^8). fp32 subnormals
+// (a < 2^-126) give k <= -134, clipped to -127.
+__device__ __forceinline__ int fp8_block_exponent(float a) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, a);
+  if (u == 0) return 0;
+  const int e_field = (int)(u >> 23);
+  if (e_field == 0) return -127;
+  const int k = e_field - 127 - 8 + ((u & 0x7FFFFFu) > 0x600000u ? 1 : 0);
+  return k < -127 ? -127 : k;
+}
+
 // Pairwise reduction with the lane 32 apart (lane l <-> l ^ 32) via v_permlane32_swap.
 __device__ __forceinline__ float max_xor32(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),

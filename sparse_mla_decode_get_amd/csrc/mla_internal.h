@@ -25,6 +25,14 @@ struct DecodeParams {
   float* part_lse;           // workspace partial lse [slots][h_q]
   uint16_t* out;             // bf16 [rows][h_q][512]
   float* lse;                // [rows][h_q]
+  // fused decode (mla_sparse_decode_fused, 128-head kernel only): RMSNorm weight and epsilon of the
+  // query rows, the rotary cos / sin of each row's 32 pairs (dims 448 + 2i, 449 + 2i), and the fp8
+  // output records [rows][h_q][528] that replace `out`
+  const uint16_t* qn_weight;  // bf16 [512]
+  float qn_eps;
+  const float* rope_cos;      // [rows][32]
+  const float* rope_sin;      // [rows][32]
+  uint8_t* out_fp8;
 };
 
 // Arguments of one decode call, as the C entry points receive them (include/mla.h).
@@ -47,6 +55,12 @@ struct DecodeCall {
   float* lse;
   void* stream;
   bool prefill = false;      // mla_sparse_prefill: no metadata, whole rows per part, no split
+  // mla_sparse_decode_fused: query transform and fp8 output (out is then uint8 [rows][h_q][528])
+  bool fused = false;
+  const void* qn_weight = nullptr;
+  float qn_eps = 0.0f;
+  const float* rope_cos = nullptr;
+  const float* rope_sin = nullptr;
 };
 
 // Where the split partials go: the caller's workspace (mla_sparse_decode), or, when fixed_bytes > 0,
@@ -75,6 +89,11 @@ int launch_combine(const float* partial, const float* partial_lse, const int32_t
                    hipStream_t stream);
 int launch_combine_bf16(const uint16_t* partial, const float* partial_lse, const int32_t* split_ptr,
                         int rows, int h_q, uint16_t* out, float* lse, hipStream_t stream);
+// Merge of the 128-head kernel's fp32 partials for the fused decode: the merged rows get the
+// conjugate rotation and are stored as fp8 records [rows][h_q][528]; single-split rows are skipped.
+int launch_combine_fused(const float* partial, const float* partial_lse, const int32_t* split_ptr,
+                         int rows, int h_q, const float* rope_cos, const float* rope_sin,
+                         uint8_t* out_fp8, float* lse, hipStream_t stream);
 int launch_dequant(const uint8_t* cache, int record_bytes, const int32_t* idx, int n,
                    uint16_t* out, hipStream_t stream);
 int launch_validate(const int32_t* idx, int64_t n, int64_t num_tokens, int32_t* bad,

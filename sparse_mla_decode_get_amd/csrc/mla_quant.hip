@@ -28,25 +28,6 @@ constexpr int kQuantWaves = 4;
 // fp8 measured fastest with one (1 GiB in: 0.40 ms per 2^20 rows against 0.43 ms with four)
 template <bool FP8> constexpr int kRowsPerWave = FP8 ? 1 : 4;
 
-// Nearest e4m3 code of a finite f32 (ties to even), saturating at +-448, sign kept.
-__device__ __forceinline__ uint32_t e4m3_code(float y) {
-  const uint32_t u = __builtin_bit_cast(uint32_t, y);
-  const uint32_t sign = (u >> 24) & 0x80u;
-  const uint32_t a = u & 0x7FFFFFFFu;
-  uint32_t code;
-  if (a < 0x3C800000u) {
-    // below 2^-6, the subnormal grid m * 2^-9 (m = 8 is the smallest normal, code 0x08)
-    code = (uint32_t)__builtin_rintf(__builtin_bit_cast(float, a) * 512.0f);
-  } else {
-    // drop 20 of the 23 mantissa bits, rounding to nearest with ties to even (a carry moves into
-    // the exponent field), then rebias the exponent from 127 to 7
-    const uint32_t r = (a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20;
-    code = r - (120u << 3);
-    code = code > 0x7Eu ? 0x7Eu : code;
-  }
-  return sign | code;
-}
-
 // Nearest e2m1 code of x / s for a finite f32 x and an e4m3 scale value s > 0 (ties to even),
 // saturating at +-6, sign kept. The magnitude code counts the midpoints 0.25, 0.75, 1.25, 1.75,
 // 2.5, 3.5, 5 (times s) below |x|; at a midpoint the even code wins (0.25 -> 0, 0.75 -> 2,
@@ -59,18 +40,6 @@ __device__ __forceinline__ uint32_t e2m1_code(float x, const float (&t)[7]) {
                      (uint32_t)(a >= t[3]) + (uint32_t)(a > t[4]) + (uint32_t)(a >= t[5]) +
                      (uint32_t)(a > t[6]);
   return c | ((__builtin_bit_cast(uint32_t, x) >> 28) & 8u);
-}
-
-// k = ceil(log2(a / 448)) for a finite a >= 0, clipped to [-127, 127]; 0 for a = 0. With
-// a = M * 2^E, M in [1, 2): k = E - 8 if M <= 1.75, else E - 7 (448 = 1.75 * 2^8). fp32 subnormals
-// (a < 2^-126) give k <= -134, clipped to -127.
-__device__ __forceinline__ int fp8_block_exponent(float a) {
-  const uint32_t u = __builtin_bit_cast(uint32_t, a);
-  if (u == 0) return 0;
-  const int e_field = (int)(u >> 23);
-  if (e_field == 0) return -127;
-  const int k = e_field - 127 - 8 + ((u & 0x7FFFFFu) > 0x600000u ? 1 : 0);
-  return k < -127 ? -127 : k;
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }

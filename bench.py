@@ -12,12 +12,15 @@ stream larger than the Infinity Cache, and uses one set.
 Prints one JSON line: TFLOP/s over valid selected tokens (2 * h_q * (512 + 512) flops per valid
 token and row), KV GB/s, the roofline block for the decode kernel, and the CPU oracle baseline.
 
-The defaults time 2000 back-to-back steps after 300 warm-up steps: right after an idle period the
-GPU's power management holds the decode kernel about 20% below its sustained rate for roughly the
-first 100 launches (~15 ms), so a short run would measure that transient rather than a decode
-loop's steady state.
+Right after an idle period the GPU's power management holds the decode kernel about 20% below its
+sustained rate for roughly the first 100 launches (~15 ms). Before the --warmup steps, every mode
+therefore runs untimed steps of the same call for --prewarm-s seconds of wall time (0.3 s by
+default; the JSON line reports the time and step count as prewarm_s and prewarm_steps), so that
+even a short timed run measures a decode loop's steady state rather than that transient. The timed
+region is unchanged: exactly --steps calls, bracketed by HIP events on the launch stream.
 
-  python bench.py [--gpus 1] [--steps 2000] [--warmup 300] [--config 2] [--no-cpu-baseline]
+  python bench.py [--gpus 1] [--steps 2000] [--warmup 300] [--prewarm-s 0.3] [--config 2]
+                  [--no-cpu-baseline]
 """
 import argparse
 import hashlib
@@ -96,6 +99,20 @@ def cpu_baseline(w, seconds: float):
                       f"{dt:.1f} s wall, float64 NumPy oracle on the host; KV {kv / dt / 1e9:.3f} GB/s"}
 
 
+def prewarm(step, seconds: float):
+    """Untimed calls of `step` until `seconds` of wall time have passed (synchronizing every 32
+    calls), to bring the GPU's clocks out of their idle state. Returns (elapsed seconds, calls)."""
+    import torch
+    t0 = time.perf_counter()
+    k = 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(32):
+            step(k)
+            k += 1
+        torch.cuda.synchronize()
+    return time.perf_counter() - t0, k
+
+
 def bench_quantize(args):
     """The cache writer: one step quantizes `--tokens` bf16 latents (N(0,1) per 32-value block times
     2^u, u ~ U(-4, 4)) into records scattered to random distinct token slots of a pool twice that
@@ -120,6 +137,7 @@ def bench_quantize(args):
         x, slots = sets[k % 2]
         mla.quantize_records(x, rec, cache=cache, slots=slots)
 
+    pw_s, pw_n = prewarm(step, args.prewarm_s)
     for k in range(args.warmup):
         step(k)
     stream = torch.cuda.current_stream(dev)
@@ -137,7 +155,7 @@ def bench_quantize(args):
         "metric": f"cache writer GB/s, bf16 -> {rec} B records", "value": gbs, "unit": "GB/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-        "data": "synthetic",
+        "data": "synthetic", "prewarm_s": pw_s, "prewarm_steps": pw_n,
         "config": {"workload": f"quantize {n} bf16 latents into {rec} B records at random slots of a "
                                f"{2 * n}-token pool", "tokens": n, "record_bytes": rec},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -170,6 +188,7 @@ def bench_prefill(args):
     def step(k):
         mla.sparse_prefill(q, k_cache, idx[k % 2], w["softmax_scale"], out=out, lse=lse)
 
+    pw_s, pw_n = prewarm(step, args.prewarm_s)
     for k in range(args.warmup):
         step(k)
     stream = torch.cuda.current_stream(dev)
@@ -188,7 +207,7 @@ def bench_prefill(args):
         "metric": "sparse MLA prefill TFLOP/s, fp8 528B/tok, H=128 topk=2048", "value": tflops,
         "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16", "data": "synthetic",
+        "dtype": "bf16", "data": "synthetic", "prewarm_s": pw_s, "prewarm_steps": pw_n,
         "config": {"workload": f"sparse prefill: {s_q} query rows, h_q {h}, topk {topk} over a "
                                "65536-token cache, 528 B fp8 records", "seq_len_q": s_q, "h_q": h,
                    "topk": topk},
@@ -202,6 +221,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=300)
+    ap.add_argument("--prewarm-s", type=float, default=0.3,
+                    help="untimed steps for this many seconds before the warm-up steps")
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--sets", type=int, default=0,
                     help="independent index sets cycled over steps (0: enough that one cycle "
@@ -300,6 +321,7 @@ def main():
             mla.sparse_decode(q, k_cache, idx_sets[j], w["softmax_scale"], md, xc, xidx_sets[j],
                               out=out, lse=lse)
 
+    pw_s, pw_n = prewarm(step, args.prewarm_s)
     for k in range(args.warmup):
         step(k)
     torch.cuda.synchronize()
@@ -371,6 +393,8 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "prewarm_s": pw_s,
+        "prewarm_steps": pw_n,
         "ms_per_step": ms_per_step,
         "higher_is_better": True,
         "scaling": "weak",

@@ -66,8 +66,10 @@ constexpr int kTileStride = 1088;
 constexpr int kTileBytes = kSubTokens * kTileStride;    // 34816
 constexpr int kRawBytes = kFp8Chunks * kSubTokens * 16; // 16896, chunk-major [chunk][token][16 B]
 constexpr int kIdxBytes = kSubTokens * 4;     // one index slot (lanes 0..31 write it)
-// epilogue staging of the bf16 output: 32 rows of 1 KB per wave, from the start of LDS
-constexpr int kStageRow = 1024;
+// epilogue staging of the bf16 output: 32 rows of 1 KB per wave, from the start of LDS, 1032
+// bytes apart (each row moves by two banks, so 32 lanes writing 8 bytes to 32 rows hit 64
+// different banks, and a row is read contiguously)
+constexpr int kStageRow = 1032;
 constexpr int kStageBytes = 32 * kStageRow;
 constexpr int kFusedRow = kFp8Rec;            // fused decode: one fp8 record per staged head row
 static_assert(32 * kFusedRow <= kStageBytes, "the fp8 records fit the bf16 staging");
@@ -811,6 +813,14 @@ void sparse_decode_wide_kernel(DecodeParams p) {
           v_addr[4 * h + dd] = lds_addr(tiles + rw * kTileStride + 16 * (4 * dd + (c_lo ^ xr)) + 8 * (jj & 1));
       }
     }
+    // Operand base of tile slot `sl` (a constant in the unrolled fp8 loop). Offsets into slots 0
+    // and 1 fit the 16-bit DS immediate and fold into the instructions; slot 2 starts past 64 KB,
+    // so its base is formed once in a register instead of once per access.
+    auto slot_base = [&](uint32_t base, int sl) -> uint32_t {
+      uint32_t a = base + sl * kTileBytes;
+      if (sl == 2) asm volatile("" : "+v"(a));
+      return a;
+    };
     auto slot_addr = [&](const uint32_t (&base)[8], int sl, uint32_t (&out)[8]) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) out[j] = base[j] + sl * kTileBytes;
@@ -825,10 +835,18 @@ void sparse_decode_wide_kernel(DecodeParams p) {
     float m_ref_next = -__builtin_inff();     // reference for the next pass (-inf: take the first)
     f32x16 oacc[16];
     float m_ref, m_max, l_sum;
+    // fp8 pipeline: per-lane running raw maximum and probability sum, the exponent offset
+    // (-m_ref once the reference is set, 0 before) and whether it is set (wave-uniform)
+    float m_lane, l_lane, ref_off;
+    bool ref_set;
     for (int pass = 0;; ++pass) {
       m_ref = m_ref_next;
       m_max = -__builtin_inff();
       l_sum = 0.0f;
+      m_lane = -__builtin_inff();
+      l_lane = 0.0f;
+      ref_set = pass > 0;
+      ref_off = pass > 0 ? -m_ref : 0.0f;
       {
         // 0 x 0 + 0 per block, in one assembly block whose leading wait states separate the VALU
         // write of the zero operand from its first read by an MFMA (an MFMA issued right after that
@@ -921,35 +939,32 @@ void sparse_decode_wide_kernel(DecodeParams p) {
         }
       };
       // The same for the fp8 pipeline, whose scores of ignored tokens already hold the ignored
-      // score (no masking), with the scale folded into the exponent: steps 0-3 the maximum of 4 raw
-      // scores each, 4 the reference (live: the sub-tile has a valid token), 5-12 two
-      // exponentials each, 13-14 the P^T operand, 15 the sum.
+      // score (no masking), with the scale folded into the exponent. The maximum and the sum are
+      // kept per lane over the whole segment and reduced across the lane pair once, after the
+      // loop: steps 0-3 fold 4 raw scores each into the lane's running maximum; step 4 takes the
+      // reference on the first live sub-tile (a wave-uniform branch, so the cross-lane reduction
+      // runs once per segment); steps 5-12 two exponentials each, added to the lane's sum in
+      // fp32; 13-14 the P^T operand of one token half each.
       auto softmax_step_fp8 = [&](SoftmaxTemps& st, int step, const f32x16& sv, bool live,
                                   bf16x8 (&pb)[2]) {
         float (&e)[16] = st.e;
-        float& mx = st.mx;
-        float& ls = st.ls;
         if (step < 4) {
           const int r = 4 * step;
-          if (step == 0) {
-            mx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), sv[2]), sv[3]);
-            ls = 0.0f;
-          } else {
-            mx = fmaxf(fmaxf(mx, sv[r]), sv[r + 1]);
-            mx = fmaxf(fmaxf(mx, sv[r + 2]), sv[r + 3]);
-          }
+          asm("v_max3_f32 %0, %0, %1, %2" : "+v"(m_lane) : "v"(sv[r]), "v"(sv[r + 1]));
+          asm("v_max3_f32 %0, %0, %1, %2" : "+v"(m_lane) : "v"(sv[r + 2]), "v"(sv[r + 3]));
         } else if (step == 4) {
-          // the scale is positive: the maximum of the scaled scores is the scaled maximum
-          mx = max_xor32(mx) * p.scale_log2;
-          m_max = live ? fmaxf(m_max, mx) : m_max;
-          m_ref = (live && m_ref == -__builtin_inff()) ? mx : m_ref;
-          // while no valid token has been seen (m_ref = -inf) every score is the ignored score
-          mx = m_ref == -__builtin_inff() ? 0.0f : -m_ref;   // reused as the exponent offset
+          // before the first live sub-tile every score is the ignored score and every lane's
+          // maximum is that score: the reduction then gives this sub-tile's own maximum
+          if (!ref_set && live) {
+            m_ref = max_xor32(m_lane) * p.scale_log2;    // the scale is positive
+            ref_off = -m_ref;
+            ref_set = true;
+          }
         } else if (step < 13) {
 #pragma unroll
           for (int r = 2 * (step - 5); r < 2 * (step - 5) + 2; ++r) {
-            e[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[r], p.scale_log2, mx));
-            ls += e[r];
+            e[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[r], p.scale_log2, ref_off));
+            l_lane += e[r];
           }
         } else if (step < 15) {
           const int ks = step - 13;
@@ -968,8 +983,6 @@ void sparse_decode_wide_kernel(DecodeParams p) {
           }
           const u32x4 packed = {xw[0], xw[1], yw[0], yw[1]};
           pb[ks] = __builtin_bit_cast(bf16x8, packed);
-        } else if (step == 15) {
-          l_sum += sum_xor32(ls);
         }
       };
       auto softmax = [&](const f32x16& sv, uint32_t mask, bf16x8 (&pb)[2]) {
@@ -1001,8 +1014,8 @@ void sparse_decode_wide_kernel(DecodeParams p) {
         // already hold the first three K operands
         // K of step kk at ka[kk % 2] + 64 (kk / 2), V of PV step n at va[h] + 16 kTileStride (n / 16)
         // + 64 (n % 16), h = 0, 1
-        const uint32_t ka[2] = {k_addr[0] + r1 * kTileBytes, k_addr[1] + r1 * kTileBytes};
-        const uint32_t va[2] = {v_addr[0] + r0 * kTileBytes, v_addr[4] + r0 * kTileBytes};
+        const uint32_t ka[2] = {slot_base(k_addr[0], r1), slot_base(k_addr[1], r1)};
+        const uint32_t va[2] = {slot_base(v_addr[0], r0), slot_base(v_addr[4], r0)};
         auto read_v = [&](int n) {
           const uint32_t off = 16 * kTileStride * (n >> 4) + 64 * (n & 15);
           return lds_v(va[0] + off, va[1] + off);
@@ -1112,6 +1125,7 @@ void sparse_decode_wide_kernel(DecodeParams p) {
         }
 
         // phase B: PV of sub-tile s with the softmax of sub-tile s+1
+        const uint32_t kb_next[2] = {slot_base(k_addr[0], r2), slot_base(k_addr[1], r2)};
         bf16x8 pb_new[2];
         SoftmaxTemps st;
 #pragma unroll
@@ -1131,7 +1145,7 @@ void sparse_decode_wide_kernel(DecodeParams p) {
           }
           if (i >= 32 - kAhead) {
             const int kk = i - (32 - kAhead);
-            kb[kk] = lds_k(k_addr[kk & 1] + r2 * kTileBytes + 64 * (kk >> 1));
+            kb[kk] = lds_k(kb_next[kk & 1] + 64 * (kk >> 1));
           }
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -1217,16 +1231,40 @@ void sparse_decode_wide_kernel(DecodeParams p) {
         s_first = -1;
       }
 
+      auto rotate = [&]() {
+        mk0 = mk1;
+        mk1 = mk2;
+        mk2 = mk3;
+        mk3 = mk4;
+        mk4 = 0;
+        const int r_old = r0;
+        r0 = r1;
+        r1 = r2;
+        r2 = r_old;
+      };
+      if constexpr (!EXTRA) {
+        // Iteration s works on slots s % 3, (s+1) % 3, (s+2) % 3; starting from s = -1, three
+        // iterations with constant slots repeat, so every slot offset is a compile-time constant.
+        // Each iteration's wait and barrier are issued by the previous iteration (every iteration
+        // issues one index load and kGatherFp8 gather copies) or before the loop.
 #pragma clang loop unroll(disable)
-      for (int s = s_first; s < nsub; ++s) {
+        for (int s = s_first; s < nsub; s += 3) {
+          fp8_iteration(s, 2, 0, 1);
+          rotate();
+          if (s + 1 >= nsub) break;
+          fp8_iteration(s + 1, 0, 1, 2);
+          rotate();
+          if (s + 2 >= nsub) break;
+          fp8_iteration(s + 2, 1, 2, 0);
+          rotate();
+        }
+      }
+#pragma clang loop unroll(disable)
+      for (int s = s_first; EXTRA && s < nsub; ++s) {
         // Top of iteration s: idx(s+4) and the gather of sub-tile s+2 (issued in iteration s-2)
         // have landed once only iteration s-1's operations (idx(s+5), gather(s+3)) may still be
         // pending.
-        if constexpr (!EXTRA) {
-          // the iteration's wait and barrier are issued by the previous iteration (every
-          // iteration issues one index load and kGatherFp8 gather copies) or before the loop
-          fp8_iteration(s, r0, r1, r2);
-        } else {
+        {
           wait_and_barrier(1 + gather_count(s + 3));
           load_indices(s + 6, (s + 6) % 3);
           if (s + 4 >= 0 && s + 4 < nsub) mk4 = gather(s + 4);
@@ -1247,22 +1285,19 @@ void sparse_decode_wide_kernel(DecodeParams p) {
           if (do_qk) softmax(s_new, mk1, pb_cur);
           if (s + 2 >= 0 && s + 2 < nsub && mk2 != 0) dequant(s + 2, mk2);
         }
-
-        mk0 = mk1;
-        mk1 = mk2;
-        mk2 = mk3;
-        mk3 = mk4;
-        mk4 = 0;
-        const int r_old = r0;
-        r0 = r1;
-        r1 = r2;
-        r2 = r_old;
+        rotate();
       }
       // O is read by VALU instructions below: 20 wait states after the last PV MFMA, which writes
       // block 15 (every other block was written at least one MFMA, 32 cycles, earlier).
       // The last iterations' copies (dummy gathers and index loads past the segment) are awaited
       // here, before this workgroup's LDS is reused or released.
       asm volatile("s_waitcnt vmcnt(0)\n\ts_nop 15\n\ts_nop 3" : "+a"(oacc[15]) :: "memory");
+      if constexpr (!EXTRA) {
+        // the fp8 pipeline's per-lane state, reduced over the lane pair of each head; with no live
+        // sub-tile the reference was never set, every probability was 0 and no pass is repeated
+        m_max = ref_set ? max_xor32(m_lane) * p.scale_log2 : -__builtin_inff();
+        l_sum = sum_xor32(l_lane);
+      }
 
       // A second pass is needed when some head's probabilities relative to m_ref could have
       // overflowed; the decision has to be the same for the whole workgroup. After the second
@@ -1275,8 +1310,9 @@ void sparse_decode_wide_kernel(DecodeParams p) {
       const bool any_big = __ballot(m_max > m_ref + kRefSlack) != 0;   // all lanes vote
       if (lane_id() == 0) redo_flags[wave] = any_big ? 1 : 0;
       wait_and_barrier(0);
+      // (the flags are written again only after this segment's next pass or the next segment's
+      // first, many barriers later, so no second barrier is needed before they are reused)
       const bool redo = (redo_flags[0] | redo_flags[1] | redo_flags[2] | redo_flags[3]) != 0;
-      wait_and_barrier(0);                    // everyone has read the flags
       if (!redo) break;
       m_ref_next = m_max;
     }
@@ -1352,10 +1388,11 @@ void sparse_decode_wide_kernel(DecodeParams p) {
         }
       } else if (final_out) {
         // Final rows in bf16, staged through LDS so that every store writes one head's 1 KB row:
-        // the wave's 32 rows go to its own 32 KB (the tiles and the start of the raw slots, free
-        // after the pass), 8-byte unit u of row h at unit u ^ h (free of bank conflicts both
-        // when written by head and when read along a row).
+        // the wave's 32 rows go to its own kStageBytes (the tiles and the start of the raw slots,
+        // free after the pass); 8-byte unit u (dims 4u .. 4u+3) of head h at h * kStageRow + 8u.
+        // Every LDS address is a per-lane base plus an immediate.
         char* const stage = smem + wave * kStageBytes;
+        const uint32_t wbase = lds_addr(stage + h * kStageRow + 8 * g);
 #pragma unroll
         for (int d = 0; d < 16; ++d) {
 #pragma unroll
@@ -1363,16 +1400,16 @@ void sparse_decode_wide_kernel(DecodeParams p) {
             bf16x4 o;
 #pragma unroll
             for (int i = 0; i < 4; ++i) o[i] = (__bf16)(oacc[d][4 * jb + i] * inv);
-            *reinterpret_cast<lds_bf16x4_w*>(lds_addr(stage + h * kStageRow + 8 * ((8 * d + 2 * jb + g) ^ h))) = o;
+            *reinterpret_cast<lds_bf16x4_w*>(wbase + 64 * d + 16 * jb) = o;
           }
-          __builtin_amdgcn_sched_barrier(0);
         }
-        // row r: lane l moves dims 8l .. 8l+7 (units 2l, 2l+1)
+        // row r: lane l moves dims 8l .. 8l+7 (units 2l, 2l+1), stored from a uniform row address
+        const uint32_t rbase = lds_addr(stage + 16 * lane);
+        char* const orow = reinterpret_cast<char*>(p.out) + ((int64_t)row * p.h_q + head_base) * (2 * kHeadDim);
         for (int r = 0; r < 32 && head_base + r < p.h_q; ++r) {
-          const char* src = stage + r * kStageRow;
-          const bf16x4 lo = *reinterpret_cast<const lds_bf16x4_w*>(lds_addr(src + 8 * ((2 * lane) ^ r)));
-          const bf16x4 hi = *reinterpret_cast<const lds_bf16x4_w*>(lds_addr(src + 8 * ((2 * lane + 1) ^ r)));
-          *reinterpret_cast<bf16x8*>(p.out + ((int64_t)row * p.h_q + head_base + r) * kHeadDim + 8 * lane) =
+          const bf16x4 lo = *reinterpret_cast<const lds_bf16x4_w*>(rbase + r * kStageRow);
+          const bf16x4 hi = *reinterpret_cast<const lds_bf16x4_w*>(rbase + r * kStageRow + 8);
+          *reinterpret_cast<bf16x8*>(orow + r * (2 * kHeadDim) + 16 * lane) =
               __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         }
       } else if (head < p.h_q) {

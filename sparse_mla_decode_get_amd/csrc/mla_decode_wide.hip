@@ -158,6 +158,24 @@ __device__ __forceinline__ void copy4_to_lds_masked(const void* gptr, uint32_t l
       : "memory");
 }
 
+// 4-byte buffer -> LDS copy by the lanes in `lanes` (wave-uniform, never 0): lane l writes LDS
+// bytes m0 + 4 * lane from byte `voff` of the buffer described by `rsrc`; offsets at or past its
+// size read nothing from memory and return 0.
+__device__ __forceinline__ void buffer_copy4_to_lds(u32x4 rsrc, uint32_t voff, uint32_t lds_base,
+                                                    uint64_t lanes) {
+  uint64_t saved_exec;
+  asm volatile(
+      "s_mov_b64 %0, exec\n\t"
+      "s_mov_b64 exec, %4\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dword %2, %3, 0 offen lds\n\t"
+      "s_mov_b64 exec, %0"
+      : "=&s"(saved_exec)
+      : "s"(lds_base), "v"(voff), "s"(rsrc), "s"(lanes)
+      : "memory");
+}
+
 // One MFMA step as an assembly statement: QK^T (scores in VGPRs, chained) and PV (O in the
 // accumulation registers). Used where other work is interleaved between the steps.
 __device__ __forceinline__ void mfma_qk_first(f32x16& s, const bf16x8& k, const bf16x8& q) {
@@ -202,6 +220,9 @@ __device__ __forceinline__ int tile_xor(int r) { return (((r >> 1) ^ (r >> 3)) &
 
 __device__ __forceinline__ u32x4 lds_read16(const char* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void lds_write16(char* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+__device__ __forceinline__ void lds_write16_at(uint32_t a, u32x4 v) {
+  *(__attribute__((address_space(3))) u32x4*)(uintptr_t)a = v;
+}
 
 // Where sub-tile j of a row segment starting at unit t0 lives in the index arrays.
 struct SubTile {
@@ -821,6 +842,34 @@ void sparse_decode_wide_kernel(DecodeParams p) {
       if (sl == 2) asm volatile("" : "+v"(a));
       return a;
     };
+    // fp8 pipeline, per-lane constants (opaque, so that they are kept rather than rebuilt):
+    //  dq_w[m]  tile slot 0 address of this lane's bf16 chunk 2 c0 + j, j % 4 = m (the swizzle
+    //           permutes chunks within groups of four): chunk 2 c0 + j is at dq_w[j % 4] + 64 (j / 4);
+    //  raw_r    raw slot 0 address of the lane's first fp8 chunk (c0, token t); chunk c0 + cc at
+    //           + 512 cc;  raw_s  the lane's two scale bytes (c0 / 2, token t);
+    //  idx_r    index slot 0 entry of token t;  idx_v  its byte offset in a 32-entry index block;
+    //  g_base / g_zb   record byte 32 w + 16 hh (this lane's first copied chunk) of record 0 of
+    //           the cache and of the zero record.
+    uint32_t dq_w[4], raw_r, raw_s, idx_r, idx_v;
+    uint64_t g_base, g_zb;
+    {
+      const int lane = lane_id();
+      const int t = lane & 31, hh = lane >> 5;
+      const int sw = tile_xor(t);
+      const int c0 = 8 * wave + 4 * hh;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) dq_w[m] = lds_addr(tiles + t * kTileStride + 32 * c0 + 16 * (m ^ sw));
+      raw_r = lds_addr(raws + (c0 * kSubTokens + t) * 16);
+      raw_s = lds_addr(raws + (32 * kSubTokens + t) * 16 + c0 / 2);
+      idx_r = lds_addr(idx_ring + 4 * t);
+      idx_v = 4 * t;
+      g_base = (uint64_t)(uintptr_t)(p.kc + 32 * wave + 16 * hh);
+      g_zb = (uint64_t)(uintptr_t)(g_zero.bytes + 32 * wave + 16 * hh);
+      asm volatile("" : "+v"(dq_w[0]), "+v"(dq_w[1]), "+v"(dq_w[2]), "+v"(dq_w[3]), "+v"(raw_r),
+                   "+v"(raw_s), "+v"(idx_r), "+v"(idx_v), "+v"(g_base), "+v"(g_zb));
+    }
+    // byte address of the segment row's index entries (the buffer base of the index loads)
+    const uint64_t idx_row = (uint64_t)(uintptr_t)(p.idx + (int64_t)row * p.topk);
     auto slot_addr = [&](const uint32_t (&base)[8], int sl, uint32_t (&out)[8]) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) out[j] = base[j] + sl * kTileBytes;
@@ -1008,8 +1057,6 @@ void sparse_decode_wide_kernel(DecodeParams p) {
       // an all-invalid mask: they gather from a valid dummy address, dequantize to zeros, get zero
       // probabilities and add nothing.
       auto fp8_iteration = [&](int s, int r0, int r1, int r2) {
-        const int lane = lane_id();
-        const int t = lane & 31, hh = lane >> 5;
         // operand addresses: K of sub-tile s+1 (phase A), V of sub-tile s (phase B); kb[0..2]
         // already hold the first three K operands
         // K of step kk at ka[kk % 2] + 64 (kk / 2), V of PV step n at va[h] + 16 kTileStride (n / 16)
@@ -1027,22 +1074,22 @@ void sparse_decode_wide_kernel(DecodeParams p) {
         // and the B operand: lane l (head l%32, dims 8(l/32) ..) holds the ignored score in dim 1.
         // Both are rebuilt every iteration instead of occupying registers.
         bf16x8 kflag, qflag;
-        // dequantization of s+2: this lane's 4 chunks of 16 values
-        const char* draw = raws + r2 * kRawBytes;
-        char* trow = tiles + r2 * kTileBytes + t * kTileStride;
-        const int sw = tile_xor(t);
-        const int c0 = 8 * wave + 4 * hh;
+        // dequantization of s+2 (raw slot r2 -> tile slot r2): this lane's 4 chunks of 16 values,
+        // two in registers at a time
+        const uint32_t draw = raw_r + r2 * kRawBytes;
+        uint32_t dqa[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) dqa[m] = slot_base(dq_w[m], r2);
         uint32_t sc2 = 0;
-        u32x4 rr[4];
+        u32x4 rr0, rr1;
         bf16x8 dlo, dhi;
-        // gather of s+4
-        const bool g_live = s + 4 < nsub && p.topk > 0;
+        // gather of s+4 (index slot r1 -> raw slot r1): tokens t < g_lim of the sub-tile are in
+        // the index row (none past the live segment)
         const int g_pos0 = kUnitTokens * t0 + kSubTokens * (s + 4);   // fp8 sub-tile s+4
-        const char* gidx = idx_ring + r1 * kIdxBytes;
+        const int g_lim = (s + 4 < nsub && p.topk > g_pos0) ? p.topk - g_pos0 : 0;
         const uint32_t graw = __builtin_amdgcn_readfirstlane(lds_addr(raws + r1 * kRawBytes));
         int gv = 0;
-        const uint8_t* grec = nullptr;
-        const uint8_t* gdat = nullptr;
+        uint64_t gdat = 0;
 #pragma unroll
         for (int i = 0; i < 32; ++i) {
           // operands are read kAhead MFMAs ahead, into phase B's first V operands at the end
@@ -1065,32 +1112,34 @@ void sparse_decode_wide_kernel(DecodeParams p) {
                          : "+v"(s_acc) : "v"(kflag), "v"(qflag));
           }
           if (i == 1) {
-            sc2 = *reinterpret_cast<const uint16_t*>(draw + (32 * kSubTokens + t) * 16 + c0 / 2);
-            rr[0] = lds_read16(draw + ((c0 + 0) * kSubTokens + t) * 16);
-            rr[1] = lds_read16(draw + ((c0 + 1) * kSubTokens + t) * 16);
-            gv = *reinterpret_cast<const int*>(gidx + 4 * t);
-          } else if (i == 2) {
-            rr[2] = lds_read16(draw + ((c0 + 2) * kSubTokens + t) * 16);
-            rr[3] = lds_read16(draw + ((c0 + 3) * kSubTokens + t) * 16);
+            sc2 = *reinterpret_cast<const __attribute__((address_space(3))) uint16_t*>(
+                (uintptr_t)(raw_s + r2 * kRawBytes));
+            rr0 = *(lds_u32x4*)(uintptr_t)(draw);
+            rr1 = *(lds_u32x4*)(uintptr_t)(draw + 512);
+            gv = *reinterpret_cast<const __attribute__((address_space(3))) int*>(
+                (uintptr_t)(idx_r + r1 * kIdxBytes));
           } else if (i == 3) {
-            const bool valid = g_live && g_pos0 + t < p.topk && gv >= 0;
+            const bool valid = idx_v < (uint32_t)(4 * g_lim) && gv >= 0;
             mk4 = (uint32_t)__ballot(valid);
             // ignored tokens and sub-tiles outside the segment read the zero record, so every copy
             // below is always issued
-            grec = valid ? p.kc + (int64_t)gv * kFp8Rec : g_zero.bytes;
-            gdat = grec + 32 * wave + 16 * hh;               // chunk 2(w + 4i) + hh at +128 i
+            const uint64_t a = g_base + (uint64_t)(int64_t)gv * kFp8Rec;
+            gdat = valid ? a : g_zb;                         // chunk 2(w + 4i) + hh at +128 i
           }
           // gather copies at steps 4..8: 4 chunk pairs (wave w moves chunks 2(w + 4c) + hh of all 32
-          // tokens) and the scale chunks of tokens 8w .. 8w+7
+          // tokens) and the scale chunks of tokens 8w .. 8w+7 (lanes of the first half: the
+          // record's byte 512 is 512 - 32 w past gdat there)
           if (i >= 4 && i < 8) {
             const int c = i - 4;
             const uint32_t dst = __builtin_amdgcn_readfirstlane(graw + 1024 * (wave + 4 * c));
-            if (c == 0) copy16_to_lds_off<0>(gdat, dst);
-            else if (c == 1) copy16_to_lds_off<128>(gdat, dst);
-            else if (c == 2) copy16_to_lds_off<256>(gdat, dst);
-            else copy16_to_lds_off<384>(gdat, dst);
+            const void* gp = (const void*)(uintptr_t)gdat;
+            if (c == 0) copy16_to_lds_off<0>(gp, dst);
+            else if (c == 1) copy16_to_lds_off<128>(gp, dst);
+            else if (c == 2) copy16_to_lds_off<256>(gp, dst);
+            else copy16_to_lds_off<384>(gp, dst);
           } else if (i == 8) {
-            copy16_to_lds_masked(grec + 512, __builtin_amdgcn_readfirstlane(graw + 32 * 512), scale_lanes_fp8);
+            copy16_to_lds_masked((const void*)(uintptr_t)(gdat + (uint64_t)(512 - 32 * wave)),
+                                 __builtin_amdgcn_readfirstlane(graw + 32 * 512), scale_lanes_fp8);
           }
           if (i == 29 && mk1 != 0xFFFFFFFFu) {
             // (the B operand's dim 9 in lanes 32..63 also holds the ignored score; A is 0 there)
@@ -1102,29 +1151,36 @@ void sparse_decode_wide_kernel(DecodeParams p) {
             qflag = __builtin_bit_cast(bf16x8, u32x4{g0, 0u, 0u, 0u});
           }
           if (i == 26) {
-            // index load of sub-tile s+6 (fp8: positions 64 t0 + 32 (s+6) ..; past the segment or
-            // for an empty selection it reads the schedule instead, a valid address)
-            const int j = s + 6;
-            const int32_t* src = p.sched;
-            if (j < nsub && p.topk > 0)
-              src = p.idx + (int64_t)row * p.topk + min(kUnitTokens * t0 + kSubTokens * j + lane_id(), p.topk - 1);
-            copy4_to_lds_masked(src, __builtin_amdgcn_readfirstlane(lds_addr(idx_ring + r0 * kIdxBytes)),
+            // index load of sub-tile s+6 (positions 64 t0 + 32 (s+6) + t) into index slot r0 from a
+            // buffer that ends at the index row's end, or is empty past the live segment
+            const int pos = kUnitTokens * t0 + kSubTokens * (s + 6);
+            const int n_in = (s + 6 < nsub && p.topk > pos) ? p.topk - pos : 0;
+            const uint64_t base = idx_row + (uint64_t)(4 * (int64_t)pos);
+            const u32x4 rsrc = {(uint32_t)base, (uint32_t)(base >> 32) & 0xFFFFu, (uint32_t)(4 * n_in),
+                                0x00020000u};
+            buffer_copy4_to_lds(rsrc, idx_v, __builtin_amdgcn_readfirstlane(lds_addr(idx_ring + r0 * kIdxBytes)),
                                 0xFFFFFFFFull);
           }
+          // the second pair of raw chunks, once the first pair's values are converted
+          if (i == 10) rr0 = *(lds_u32x4*)(uintptr_t)(draw + 1024);
+          if (i == 14) rr1 = *(lds_u32x4*)(uintptr_t)(draw + 1536);
           if (i >= 8 && i < 24) {
             const int cc = (i - 8) >> 2, part = (i - 8) & 3;
             const uint32_t sb = (sc2 >> (8 * (cc >> 1))) & 0xFFu;
-            if (part == 0) dlo = dequant_fp8_8(rr[cc][0], rr[cc][1], sb);
-            else if (part == 1) dhi = dequant_fp8_8(rr[cc][2], rr[cc][3], sb);
+            const u32x4& r = (cc & 1) ? rr1 : rr0;
+            if (part == 0) dlo = dequant_fp8_8(r[0], r[1], sb);
+            else if (part == 1) dhi = dequant_fp8_8(r[2], r[3], sb);
             else if (part == 2) {
-              lds_write16(trow + 16 * ((2 * (c0 + cc)) ^ sw), __builtin_bit_cast(u32x4, dlo));
-              lds_write16(trow + 16 * ((2 * (c0 + cc) + 1) ^ sw), __builtin_bit_cast(u32x4, dhi));
+              // bf16 chunks j = 2 cc (dlo) and 2 cc + 1 (dhi)
+              lds_write16_at(dqa[(2 * cc) & 3] + 64 * ((2 * cc) >> 2), __builtin_bit_cast(u32x4, dlo));
+              lds_write16_at(dqa[(2 * cc + 1) & 3] + 64 * ((2 * cc + 1) >> 2), __builtin_bit_cast(u32x4, dhi));
             }
           }
           __builtin_amdgcn_sched_barrier(0);
         }
 
-        // phase B: PV of sub-tile s with the softmax of sub-tile s+1
+        // phase B: PV of sub-tile s with the softmax of sub-tile s+1. The P^T operand of the first
+        // token half replaces pb_cur[0] (last read by PV step 15) as soon as it is built.
         const uint32_t kb_next[2] = {slot_base(k_addr[0], r2), slot_base(k_addr[1], r2)};
         bf16x8 pb_new[2];
         SoftmaxTemps st;
@@ -1136,6 +1192,7 @@ void sparse_decode_wide_kernel(DecodeParams p) {
           // MFMA (the PV MFMA above runs meanwhile)
           if (i == 0) asm volatile("s_nop 15\n\ts_nop 3" : "+v"(s_acc));
           if ((i & 1) == 0) softmax_step_fp8(st, i >> 1, s_acc, mk1 != 0, pb_new);   // steps 0..15
+          if (i == 26) pb_cur[0] = pb_new[0];
           if (i == 32 - kAhead) {
             // Start of iteration s+1, while the last PV MFMAs (operands already read) still run:
             // every V read of this iteration is complete, idx(s+5) and the gather of s+3 (issued
@@ -1149,7 +1206,6 @@ void sparse_decode_wide_kernel(DecodeParams p) {
           }
           __builtin_amdgcn_sched_barrier(0);
         }
-        pb_cur[0] = pb_new[0];
         pb_cur[1] = pb_new[1];
       };
 

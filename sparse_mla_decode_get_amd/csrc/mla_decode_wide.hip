@@ -1087,7 +1087,8 @@ void sparse_decode_wide_kernel(DecodeParams p) {
         // the index row (none past the live segment)
         const int g_pos0 = kUnitTokens * t0 + kSubTokens * (s + 4);   // fp8 sub-tile s+4
         const int g_lim = (s + 4 < nsub && p.topk > g_pos0) ? p.topk - g_pos0 : 0;
-        const uint32_t graw = __builtin_amdgcn_readfirstlane(lds_addr(raws + r1 * kRawBytes));
+        // LDS byte addresses formed from the array itself (no generic-pointer null check)
+        const uint32_t graw = lds_addr(smem) + kOffRaw + r1 * kRawBytes;
         int gv = 0;
         uint64_t gdat = 0;
 #pragma unroll
@@ -1100,6 +1101,9 @@ void sparse_decode_wide_kernel(DecodeParams p) {
             const int n = i + kAhead - 32;                  // phase B's first V operands
             vb[n % kRing] = read_v(n);
           }
+          // operands are awaited in pairs: before an even step, the next step's operand too, so
+          // that every other step needs no wait of its own
+          if ((i & 1) == 0) asm volatile("" ::"v"(kb[(i + 1) % kRing]));
           if (i == 0) mfma_qk_first(s_acc, kb[0], qreg[0]);
           else mfma_qk(s_acc, kb[i % kRing], qreg[i]);
           // extra k-step after the last one: the ignored score for ignored tokens of s+1, +0 for
@@ -1158,7 +1162,7 @@ void sparse_decode_wide_kernel(DecodeParams p) {
             const uint64_t base = idx_row + (uint64_t)(4 * (int64_t)pos);
             const u32x4 rsrc = {(uint32_t)base, (uint32_t)(base >> 32) & 0xFFFFu, (uint32_t)(4 * n_in),
                                 0x00020000u};
-            buffer_copy4_to_lds(rsrc, idx_v, __builtin_amdgcn_readfirstlane(lds_addr(idx_ring + r0 * kIdxBytes)),
+            buffer_copy4_to_lds(rsrc, idx_v, lds_addr(smem) + kOffIdx + (wave * kStages + r0) * kIdxBytes,
                                 0xFFFFFFFFull);
           }
           // the second pair of raw chunks, once the first pair's values are converted
@@ -1187,6 +1191,7 @@ void sparse_decode_wide_kernel(DecodeParams p) {
 #pragma unroll
         for (int i = 0; i < 32; ++i) {
           if (i + kAhead < 32) vb[(i + kAhead) % kRing] = read_v(i + kAhead);
+          if ((i & 1) == 0) asm volatile("" ::"v"(vb[(i + 1) % kRing]));
           mfma_pv(oacc[i & 15], vb[i % kRing], pb_cur[i >> 4]);
           // the scores are read by VALU instructions next: 20 wait states after the last QK^T
           // MFMA (the PV MFMA above runs meanwhile)

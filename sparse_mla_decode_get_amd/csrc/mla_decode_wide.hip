@@ -604,10 +604,31 @@ void sparse_decode_wide_kernel(DecodeParams p) {
 #pragma unroll
       for (int u = 0; u < 8; ++u) v[u] = in[u] ? v[u] : -1;
     };
+    // fp8 pipeline: gather of sub-tile j (j < 3, before the loop) from index slot j into raw slot
+    // j; sub-tiles past `live` or entries past the index row are ignored (they copy the zero
+    // record). Returns the sub-tile's validity mask.
+    auto fp8_gather_first = [&](int j, int live) -> uint32_t {
+      const int lane = lane_id();
+      const int t = lane & 31, hh = lane >> 5;
+      const int gv = *reinterpret_cast<const int*>(idx_ring + j * kIdxBytes + 4 * t);
+      const bool valid = j < live && p.topk > 0 && kUnitTokens * t0 + kSubTokens * j + t < p.topk && gv >= 0;
+      const uint32_t mask = (uint32_t)__ballot(valid);
+      const uint8_t* grec = valid ? p.kc + (int64_t)gv * kFp8Rec : g_zero.bytes;
+      const uint8_t* gdat = grec + 32 * wave + 16 * hh;
+      const uint32_t graw = lds_addr(smem) + kOffRaw + j * kRawBytes;
+      copy16_to_lds_off<0>(gdat, graw + 1024 * wave);
+      copy16_to_lds_off<128>(gdat, graw + 1024 * (wave + 4));
+      copy16_to_lds_off<256>(gdat, graw + 1024 * (wave + 8));
+      copy16_to_lds_off<384>(gdat, graw + 1024 * (wave + 12));
+      copy16_to_lds_masked(grec + 512, graw + 32 * 512, scale_lanes_fp8);
+      return mask;
+    };
+    uint32_t mk_first[3] = {0u, 0u, 0u};
     int scan_v[8];
     scan_batch(0, scan_v);
     load_indices(0, 0);                          // "iteration -6" of the first pass
     load_indices(1, 1);                          // "iteration -5"
+    if constexpr (!EXTRA) load_indices(2, 2);
 
     // ---- Q of this wave's 32 heads, B-operand layout of v_mfma_f32_32x32x16_bf16:
     // lane l holds head l%32, dims 16kk + 8(l/32) .. +7 of k-step kk. Heads past h_q load a copy
@@ -620,6 +641,19 @@ void sparse_decode_wide_kernel(DecodeParams p) {
           p.q + ((int64_t)row * p.h_q + qh) * kHeadDim + 8 * (lane >> 5));
 #pragma unroll
       for (int kk = 0; kk < 32; ++kk) qreg[kk] = __builtin_bit_cast(bf16x8, qp[2 * kk]);
+    }
+    if constexpr (!EXTRA) {
+      // The first three sub-tiles are gathered as soon as their index rows are in, while Q is
+      // still arriving: the pipeline then starts one memory latency after the Q traffic instead
+      // of two. The scan batch and idx(0 .. 2) have landed once at most the 32 Q loads issued
+      // after them are outstanding. A later segment first waits until every wave is done with the
+      // previous segment's epilogue staging, which overlaps the raw slots.
+      asm volatile("s_waitcnt vmcnt(32)" ::: "memory");
+      if (!first_seg) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+      for (int j = 0; j < 3; ++j) mk_first[j] = fp8_gather_first(j, nsub_all);
+      load_indices(3, 0);                        // the slots' entries are read (lgkmcnt waited)
+      load_indices(4, 1);
     }
     if constexpr (FUSED) {
       // Fused decode: the query row is RMS-normalised with the weight w (q / sqrt(mean(q^2) + eps)
@@ -1215,39 +1249,34 @@ void sparse_decode_wide_kernel(DecodeParams p) {
       };
 
 
-      // Iterations -4 .. -2 of the fp8 pipeline have no real QK^T or PV yet: they only gather
-      // sub-tiles 0 .. 2, load indices 2 .. 4 and (iteration -2) dequantize sub-tile 0, each ending
-      // in the same wait and barrier as a full iteration (which also issues one index load and
-      // kGatherFp8 copies), so their length is set by memory latency, not by 65 idle MFMAs.
-      auto fp8_prologue_iteration = [&](int s, int r0, int r1, int r2) {
-        const int lane = lane_id();
-        const int t = lane & 31, hh = lane >> 5;
-        const bool g_live = s + 4 < nsub && p.topk > 0;
-        const int g_pos0 = kUnitTokens * t0 + kSubTokens * (s + 4);
-        const char* gidx = idx_ring + r1 * kIdxBytes;
-        const uint32_t graw = __builtin_amdgcn_readfirstlane(lds_addr(raws + r1 * kRawBytes));
-        const int gv = *reinterpret_cast<const int*>(gidx + 4 * t);
-        const bool valid = g_live && g_pos0 + t < p.topk && gv >= 0;
-        mk4 = (uint32_t)__ballot(valid);
-        const uint8_t* grec = valid ? p.kc + (int64_t)gv * kFp8Rec : g_zero.bytes;
-        const uint8_t* gdat = grec + 32 * wave + 16 * hh;
-        copy16_to_lds_off<0>(gdat, __builtin_amdgcn_readfirstlane(graw + 1024 * wave));
-        copy16_to_lds_off<128>(gdat, __builtin_amdgcn_readfirstlane(graw + 1024 * (wave + 4)));
-        copy16_to_lds_off<256>(gdat, __builtin_amdgcn_readfirstlane(graw + 1024 * (wave + 8)));
-        copy16_to_lds_off<384>(gdat, __builtin_amdgcn_readfirstlane(graw + 1024 * (wave + 12)));
-        copy16_to_lds_masked(grec + 512, __builtin_amdgcn_readfirstlane(graw + 32 * 512), scale_lanes_fp8);
+      // The fp8 pipeline starts at iteration -1 with sub-tiles 0 .. 2 gathered and idx(3), idx(4)
+      // loaded (at the segment start, or here for a repeated pass) and sub-tile 0 dequantized.
+      if (EXTRA && pass > 0) {                   // the first pass's were issued with Q
+        load_indices(0, 0);                      // "iteration -6"
+        load_indices(1, 1);                      // "iteration -5"
+      }
+      if (!EXTRA && pass > 0) {
+        load_indices(0, 0);
+        load_indices(1, 1);
+        load_indices(2, 2);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+        for (int j = 0; j < 3; ++j) mk_first[j] = fp8_gather_first(j, nsub);
+        load_indices(3, 0);
+        load_indices(4, 1);
+      }
+
+      // slots of sub-tiles s, s+1, s+2 (s % 3 ... for s >= -4), rotated every iteration
+      int r0 = 2, r1 = 0, r2 = 1;
+      int s_first = -4;
+      if constexpr (!EXTRA) {
+        // every wave's part of sub-tile 0 has landed: dequantize it into tile slot 0
+        wait_and_barrier(0);
         {
-          const int j = s + 6;
-          const int32_t* src = p.sched;
-          if (j < nsub && p.topk > 0)
-            src = p.idx + (int64_t)row * p.topk + min(kUnitTokens * t0 + kSubTokens * j + lane, p.topk - 1);
-          copy4_to_lds_masked(src, __builtin_amdgcn_readfirstlane(lds_addr(idx_ring + r0 * kIdxBytes)),
-                              0xFFFFFFFFull);
-        }
-        if (s == -2) {
-          // sub-tile 0, gathered in iteration -4 (landed: the last barrier waited for it)
-          const char* draw = raws + r2 * kRawBytes;
-          char* trow = tiles + r2 * kTileBytes + t * kTileStride;
+          const int lane = lane_id();
+          const int t = lane & 31, hh = lane >> 5;
+          const char* draw = raws;
+          char* trow = tiles + t * kTileStride;
           const int sw = tile_xor(t);
           const int c0 = 8 * wave + 4 * hh;
           const uint32_t sc2 = *reinterpret_cast<const uint16_t*>(draw + (32 * kSubTokens + t) * 16 + c0 / 2);
@@ -1259,36 +1288,17 @@ void sparse_decode_wide_kernel(DecodeParams p) {
             lds_write16(trow + 16 * ((2 * (c0 + cc) + 1) ^ sw), __builtin_bit_cast(u32x4, dequant_fp8_8(r[2], r[3], sb)));
           }
         }
-        wait_and_barrier(1 + kGatherFp8);
-      };
-
-      if (pass > 0) {                            // the first pass's were issued with Q
-        load_indices(0, 0);                      // "iteration -6"
-        load_indices(1, 1);                      // "iteration -5"
-      }
-
-      // slots of sub-tiles s, s+1, s+2 (s % 3 ... for s >= -4), rotated every iteration
-      int r0 = 2, r1 = 0, r2 = 1;
-      int s_first = -4;
-      if constexpr (!EXTRA) {
-        // start of iteration -4: idx(0) has landed ("iteration -5" issued only idx(1))
-        wait_and_barrier(1);
-        for (int s = -4; s < -1; ++s) {
-          fp8_prologue_iteration(s, r0, r1, r2);
-          mk0 = mk1;
-          mk1 = mk2;
-          mk2 = mk3;
-          mk3 = mk4;
-          mk4 = 0;
-          const int r_old = r0;
-          r0 = r1;
-          r1 = r2;
-          r2 = r_old;
-        }
-        // the first K operands of QK^T(0) (tile 0, dequantized in iteration -2)
+        // tile 0 is complete and raw slot 0 free for the gather of sub-tile 3
+        wait_and_barrier(0);
+        mk0 = 0u;
+        mk1 = mk_first[0];
+        mk2 = mk_first[1];
+        mk3 = mk_first[2];
+        mk4 = 0u;
+        // the first K operands of QK^T(0) (tile slot 0)
 #pragma unroll
         for (int kk = 0; kk < kAhead; ++kk)
-          kb[kk] = lds_k(k_addr[kk & 1] + r1 * kTileBytes + 64 * (kk >> 1));
+          kb[kk] = lds_k(k_addr[kk & 1] + 64 * (kk >> 1));
         s_first = -1;
       }
 

@@ -257,13 +257,15 @@ void sparse_decode_kernel(DecodeParams p) {
     // Q rows of the workgroup's heads are copied once into LDS (8 head rows of 1 KB per wave, row
     // hr of half hr / 32's tile area at (hr % 32) * kQRow, free until the first dequantization) and
     // read into registers from there below, instead of every half loading all of Q from memory.
+    auto copy_q = [&]() {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int hr = 8 * wave_all + i;
-      const int qh = min(head_base + hr, p.h_q - 1);
-      const uint16_t* src = p.q + ((int64_t)row * p.h_q + qh) * kHeadDim + 8 * lane;
-      copy16_to_lds(src, __builtin_amdgcn_readfirstlane(lds_addr(q_row(hr))));
-    }
+      for (int i = 0; i < 8; ++i) {
+        const int hr = 8 * wave_all + i;
+        const int qh = min(head_base + hr, p.h_q - 1);
+        const uint16_t* src = p.q + ((int64_t)row * p.h_q + qh) * kHeadDim + 8 * lane_id();
+        copy16_to_lds(src, __builtin_amdgcn_readfirstlane(lds_addr(q_row(hr))));
+      }
+    };
     bf16x8 qreg[8][2];
 
     f32x16 oacc[C::kDB][C::kHB];
@@ -331,12 +333,22 @@ void sparse_decode_kernel(DecodeParams p) {
       return bal;
     };
 
-    // Prologue: index entries of iterations 0 .. kDepth-1 (waited for together with Q), then the
-    // gathers of those iterations, each followed by the index copy kDepth further on, as in the loop.
+    // Prologue: index entries of iterations 0 .. kDepth-1, then the Q rows; as soon as the index
+    // entries have landed (at most the 8 Q copies outstanding) the gathers of those iterations are
+    // issued, each followed by the index copy kDepth further on, as in the loop, so that their
+    // latency overlaps the Q traffic; then Q is awaited (at most the gathers' copies outstanding).
+    static_assert(kDepth * (C::kNQ + 1) == 6, "wait count of the prologue");
 #pragma unroll
     for (int k = 0; k < kDepth; ++k) load_idx(k);
-    // vmcnt(0) as a compiler-visible wait, so Q counts as resident for the rest of the segment
-    __builtin_amdgcn_s_waitcnt(0x0F70);
+    copy_q();
+    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    uint32_t mk[kDepth + 1];                          // validity masks of iterations k .. k+kDepth
+#pragma unroll
+    for (int k = 0; k < kDepth; ++k) {
+      mk[k] = gather(k);
+      load_idx(k + kDepth);
+    }
+    asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
     __syncthreads();                                  // every wave's Q rows are in LDS
     {
       // lane (t16, q4) takes dims 64c + 16*q4 .. +15 of head my_head
@@ -348,12 +360,6 @@ void sparse_decode_kernel(DecodeParams p) {
       }
       // complete before any wave can reach the first dequantization, which overwrites these rows
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    }
-    uint32_t mk[kDepth + 1];                          // validity masks of iterations k .. k+kDepth
-#pragma unroll
-    for (int k = 0; k < kDepth; ++k) {
-      mk[k] = gather(k);
-      load_idx(k + kDepth);
     }
     // The split bookkeeping is needed only by the epilogue. It is read after the segment's first
     // copies are issued, so its memory round trip overlaps theirs instead of delaying the Q load.

@@ -132,9 +132,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_fused_kernel(
     amax = fmaxf(amax, __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(
                            (lane ^ msk) << 2, __builtin_bit_cast(int, amax))));
   const int k = fp8_block_exponent(amax);
-  uint32_t w = 0u;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) w |= e4m3_code(__builtin_ldexpf(y[i], -k)) << (8 * i);
+  const uint32_t w = e4m3_codes4(y[0], y[1], y[2], y[3], k);
   uint8_t* rec = out_fp8 + ((int64_t)row * h_q + head) * kFp8Rec;
   *reinterpret_cast<uint32_t*>(rec + dim) = w;
   if ((t & 7) == 0) rec[kHeadDim + (t >> 3)] = (uint8_t)(k + 127);

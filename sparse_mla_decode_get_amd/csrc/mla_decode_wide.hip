@@ -1433,9 +1433,7 @@ void sparse_decode_wide_kernel(DecodeParams p) {
           const int k = fp8_block_exponent(a);
 #pragma unroll
           for (int rb = 0; rb < 4; ++rb) {
-            uint32_t w = 0u;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) w |= e4m3_code(__builtin_ldexpf(y[4 * rb + i], -k)) << (8 * i);
+            const uint32_t w = e4m3_codes4(y[4 * rb], y[4 * rb + 1], y[4 * rb + 2], y[4 * rb + 3], k);
             *reinterpret_cast<__attribute__((address_space(3))) uint32_t*>(
                 lds_addr(stage + h * kFusedRow + 32 * d + 8 * rb + 4 * g)) = w;
           }

@@ -97,6 +97,25 @@ __device__ __forceinline__ uint32_t e4m3_code(float y) {
   return sign | code;
 }
 
+// Four f32 values / 2^k -> four e4m3 codes (value i in byte i), with gfx950's scaled conversion:
+// it divides by its scale operand and rounds to nearest, ties to even, keeping subnormals and the
+// sign, exactly as e4m3_code does for results within +-448 (checked over every e4m3 value, every
+// midpoint and its neighbours, and random values). The caller guarantees |v / 2^k| <= 448 (beyond,
+// the conversion gives NaN rather than saturating). k = -127 has no normal f32 scale: the values
+// are doubled (exact) and divided by 2^-126.
+__device__ __forceinline__ uint32_t e4m3_codes4(float v0, float v1, float v2, float v3, int k) {
+  typedef short v2s __attribute__((ext_vector_type(2)));
+  if (k < -126) {
+    v0 *= 2.0f; v1 *= 2.0f; v2 *= 2.0f; v3 *= 2.0f;
+    k = -126;
+  }
+  const float sc = __builtin_bit_cast(float, (uint32_t)(k + 127) << 23);
+  v2s r = {0, 0};
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, v0, v1, sc, false);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, v2, v3, sc, true);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
 // k = ceil(log2(a / 448)) for a finite a >= 0, clipped to [-127, 127]; 0 for a = 0. With
 // a = M * 2^E, M in [1, 2): k = E - 8 if M <= 1.75, else E - 7 (448 = 1.75 * 2^8). fp32 subnormals
 // (a < 2^-126) give k <= -134, clipped to -127.

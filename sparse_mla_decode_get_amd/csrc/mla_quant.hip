@@ -70,10 +70,9 @@ __device__ __forceinline__ void quantize_row(const u32x4& w, int64_t tok, uint8_
     a = fmaxf(a, shfl_xor(a, lane, 1));
     a = fmaxf(a, shfl_xor(a, lane, 2));                       // block lane / 4: 32 values
     const int k = fp8_block_exponent(a);
-    uint32_t b[2] = {0u, 0u};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) b[i >> 2] |= e4m3_code(__builtin_ldexpf(v[i], -k)) << (8 * (i & 3));
-    *reinterpret_cast<u32x2*>(rec + 8 * lane) = u32x2{b[0], b[1]};
+    const uint32_t b0 = e4m3_codes4(v[0], v[1], v[2], v[3], k);
+    const uint32_t b1 = e4m3_codes4(v[4], v[5], v[6], v[7], k);
+    *reinterpret_cast<u32x2*>(rec + 8 * lane) = u32x2{b0, b1};
     // scale byte of block j is held by lane 4j; lane 16d packs blocks 4d .. 4d+3
     const uint32_t sb = (uint32_t)(k + 127);
     const uint32_t d = sb | (shfl_from(sb, lane + 4) << 8) | (shfl_from(sb, lane + 8) << 16) |

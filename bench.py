@@ -17,10 +17,13 @@ sustained rate for roughly the first 100 launches (~15 ms). Before the --warmup 
 therefore runs untimed steps of the same call for --prewarm-s seconds of wall time (0.3 s by
 default; the JSON line reports the time and step count as prewarm_s and prewarm_steps), so that
 even a short timed run measures a decode loop's steady state rather than that transient. The timed
-region is unchanged: exactly --steps calls, bracketed by HIP events on the launch stream.
+region is unchanged: exactly --steps calls, bracketed by HIP events on the launch stream. With
+--graph those calls are captured once as a HIP graph and the timed region replays it, so that steps
+shorter than the host's launch time (the mid and mixed workloads, or any run under a kernel tracer)
+measure the GPU rather than the launch rate.
 
   python bench.py [--gpus 1] [--steps 2000] [--warmup 300] [--prewarm-s 0.3] [--config 2]
-                  [--no-cpu-baseline]
+                  [--graph] [--no-cpu-baseline]
 """
 import argparse
 import hashlib
@@ -228,6 +231,8 @@ def main():
                     help="independent index sets cycled over steps (0: enough that one cycle "
                          "selects more than 512 MiB of records, at least 4)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture the timed steps as one HIP graph and replay it (decode and fused)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-probe", action="store_true",
                     help="run one 1 GiB device copy first (calibrates HBM byte counters)")
@@ -326,14 +331,28 @@ def main():
         step(k)
     torch.cuda.synchronize()
 
+    graph = None
+    if args.graph:
+        # the timed steps captured once as one HIP graph: the same --steps calls, replayed with no
+        # host launch work between them (short steps otherwise measure the host's launch rate)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for k in range(args.steps):
+                step(k)
+        graph.replay()                      # untimed first replay
+        torch.cuda.synchronize()
+
     # HIP events on the launch stream bracket the timed region only: an event recorded between
     # two launches costs the GPU several microseconds, so per-step events would time themselves
     # along with short steps
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     e0.record(stream)
-    for k in range(args.steps):
-        step(k)
+    if graph is not None:
+        graph.replay()
+    else:
+        for k in range(args.steps):
+            step(k)
     e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -416,6 +435,7 @@ def main():
         "index_set_mib_per_cycle": len(sets) * set_kv / 2**20,
         "metadata_ms": metadata_ms,
         "per_launch_ms": per_launch_ms,
+        "graph": bool(args.graph),
         "wall_s_timed": wall,
         "gen_s": t_gen,
         "kernel_source_sha256_16": kernel_source_hash(h > 64),

@@ -318,16 +318,19 @@ def test_duplicate_entries_count_with_multiplicity(h_q, extra):
         assert np.allclose(ref_lse[0], h_lse[0] + math.log(2.0), atol=1e-9)
 
 
-def test_decode_replays_from_a_captured_graph():
+@pytest.mark.parametrize("h_q", [128, 64])
+def test_decode_replays_from_a_captured_graph(h_q):
     """The decode step captured in a HIP graph (through torch.cuda.CUDAGraph): every replay, with
-    eager work on the same stream between replays, matches the eager result bit for bit."""
-    spec = Spec("graph", 4, 2, 128, 700, 4096, neg="tail10")
+    eager work on the same stream between replays, matches the eager result bit for bit. Both
+    kernels (128-head groups with fp32 partials, 64-head groups with bf16 partials) and their
+    merges are captured."""
+    spec = Spec("graph", 4, 2, h_q, 700, 4096, neg="tail10")
     w = make_workload(spec, seed=51)
     d = to_dev(w)
-    md = mla.get_metadata(4, 2, 128, 700, 0, num_parts=13)      # rows split: decode + merge
+    md = mla.get_metadata(4, 2, h_q, 700, 0, num_parts=13)      # rows split: decode + merge
     assert md.workspace is not None
-    out = torch.empty((4, 2, 128, 512), dtype=torch.bfloat16, device="cuda")
-    lse = torch.empty((4, 2, 128), dtype=torch.float32, device="cuda")
+    out = torch.empty((4, 2, h_q, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((4, 2, h_q), dtype=torch.float32, device="cuda")
     mla.sparse_decode(d["q"], d["k_cache"], d["indices"], w["softmax_scale"], md, out=out, lse=lse)
     torch.cuda.synchronize()
     eager_out, eager_lse = out.clone(), lse.clone()

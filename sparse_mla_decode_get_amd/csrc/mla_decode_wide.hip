@@ -7,25 +7,30 @@
 // natural-log lse returned beside the output.
 //
 // Layout of the work. One workgroup = 4 waves = one wave per SIMD, each wave with the full 512
-// registers of its SIMD. Wave w owns query heads 32w..32w+31 of the head group for everything:
+// registers of its SIMD. Wave w owns query heads 32w..32w+31 of the head group for QK^T and the
+// softmax:
 //   Q      bf16, 32 heads x 512 dims, 128 VGPRs (B operand of the QK^T product)
-//   O^T    fp32, 512 dims x 32 heads, 16 MFMA blocks of 32x32 = all 256 AGPRs
 //   S^T    fp32, 32 tokens x 32 heads per 32-token sub-tile, 16 VGPRs
-// so the softmax (max, exp, sum, P) never leaves the wave: P goes from the QK^T accumulator layout
-// to the PV operand layout with v_permlane32_swap, no LDS round trip and no cross-wave exchange.
+// so the softmax (max, exp, sum, P) of a head never leaves its wave: P goes from the QK^T
+// accumulator layout to the PV operand layout with v_permlane32_swap. O takes all 256 AGPRs of
+// a wave as 16 MFMA blocks of 32x32, in one of two splits:
+//   - the fp8 pipeline splits PV by dims: wave w accumulates O^T for dims 128w..128w+127 of all
+//     128 heads, so each wave reads only its quarter of the V tile (8 KB per sub-tile instead of
+//     32 KB); the P^T operands of the four head groups meet in a small LDS exchange buffer;
+//   - the extra-cache variant splits PV by heads: O^T of the wave's own 32 heads, all 512 dims.
 //
 // Each selected record is gathered once (HBM -> LDS with global_load_lds_dwordx4) and dequantized
 // once, by all four waves together (each takes 128 dims), into a bf16 tile [32 tokens][512 dims]
 // that both products read: QK^T as row reads (ds_read_b128), PV as transposed reads
 // (ds_read_b64_tr_b16). Three tiles and three raw buffers rotate through a software pipeline in
-// which iteration s, behind a single workgroup barrier,
+// which iteration s
 //   - loads the indices of sub-tile s+6 and gathers the records of sub-tile s+4,
-//   - runs QK^T of sub-tile s+1 (one assembly block: the scores land in VGPRs),
-//   - runs PV of sub-tile s (one assembly block: O stays in the accumulation registers),
+//   - runs QK^T of sub-tile s+1 (the scores land in VGPRs),
+//   - runs PV of sub-tile s (O stays in the accumulation registers),
 //   - runs the softmax of sub-tile s+1 and dequantizes sub-tile s+2.
 // The index loads and gathers are issued as inline assembly that writes LDS directly; the only
-// waits on them are the explicit vmcnt waits at the top of each iteration, whose counts follow
-// the issue order (loads complete in order).
+// waits on them are the explicit vmcnt waits at the iteration barrier, whose counts follow the
+// issue order (loads complete in order).
 
 #include "mla_device.h"
 #include "mla_internal.h"
@@ -76,10 +81,22 @@ static_assert(32 * kFusedRow <= kStageBytes, "the fp8 records fit the bf16 stagi
 constexpr int kStages = 3;
 constexpr int kOffRaw = kStages * kTileBytes;
 constexpr int kOffIdx = kOffRaw + kStages * kRawBytes;
-constexpr int kOffFlags = kOffIdx + kWaves * kStages * kIdxBytes;
-constexpr int kOffScan = kOffFlags + 16;      // per-wave last live sub-tile, two segment buffers
-constexpr int kLdsBytes = kOffScan + 2 * kWaves * 4;
-static_assert(kLdsBytes <= 160 * 1024, "LDS of one workgroup");
+// P^T exchange buffer of the fp8 pipeline: the B operand of PV for the 4 head groups and 2 token
+// halves of one sub-tile, 16 bytes per lane (head group g, half ks at 1024 (2 g + ks))
+constexpr int kPBytes = kWaves * 2 * 64 * 16;
+// The rest of the layout depends on the variant. The fp8 pipeline shares one index ring among the
+// waves (each wave loads 8 of a slot's 32 entries) and holds the P^T exchange buffer; the
+// extra-cache variant gives every wave its own ring and exchanges nothing.
+template <bool EXTRA>
+struct Lds {
+  static constexpr int kIdxSlots = EXTRA ? kWaves * kStages : kStages;
+  static constexpr int kOffFlags = kOffIdx + kIdxSlots * kIdxBytes;
+  static constexpr int kOffScan = kOffFlags + 16;   // per-wave last live sub-tile, two segment buffers
+  static constexpr int kOffP = kOffScan + 2 * kWaves * 4;
+  static constexpr int kBytes = kOffP + (EXTRA ? 0 : kPBytes);
+  static_assert(kBytes <= 160 * 1024, "LDS of one workgroup");
+  static_assert(kOffP % 16 == 0, "16-byte P^T operands");
+};
 static_assert(kWaves * kStageBytes <= kOffIdx, "the epilogue staging leaves the index ring alone");
 static_assert(16 * kTileStride + 3 * 256 + 8 < 65536, "PV operand offsets fit the DS immediate");
 // Largest allowed excess of a score over its head's probability reference, in log2 units: P stays
@@ -514,15 +531,17 @@ __device__ __forceinline__ void pv_chain(const uint32_t (&a)[8], f32x16 (&o)[16]
 template <bool EXTRA, bool FUSED>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void sparse_decode_wide_kernel(DecodeParams p) {
-  __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
+  using L = Lds<EXTRA>;
+  __shared__ __attribute__((aligned(16))) char smem[L::kBytes];
   char* const tiles = smem;
   char* const raws = smem + kOffRaw;
-  int* const redo_flags = reinterpret_cast<int*>(smem + kOffFlags);
-  int* const scan_slots = reinterpret_cast<int*>(smem + kOffScan);
+  int* const redo_flags = reinterpret_cast<int*>(smem + L::kOffFlags);
+  int* const scan_slots = reinterpret_cast<int*>(smem + L::kOffScan);
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int head_base = blockIdx.y * kGroupHeads + 32 * wave;   // this wave's first head
-  char* const idx_ring = smem + kOffIdx + wave * kStages * kIdxBytes;
+  // index ring: the wave's own (extra-cache variant) or the one all waves share (fp8 pipeline)
+  char* const idx_ring = smem + kOffIdx + (EXTRA ? wave * kStages * kIdxBytes : 0);
   // lanes of the scale-chunk copies: tokens 8w .. 8w+7 (first lane half; fp4: both halves)
   const uint64_t scale_lanes_fp8 = 0xFFull << (8 * wave);
   const uint64_t scale_lanes_fp4 = scale_lanes_fp8 | (scale_lanes_fp8 << 32);
@@ -565,16 +584,18 @@ void sparse_decode_wide_kernel(DecodeParams p) {
     // entries past the end of the index row are fetched from a clamped address and replaced by
     // -1 when read). It is issued for every iteration: past the last sub-tile, or for a selection
     // of size 0 (no index array), it reads from the schedule instead (a valid address).
+    // In the shared ring of the fp8 pipeline, wave w loads entries 8w .. 8w+7 (lanes 0..7).
     auto load_indices = [&](int j, int slot) {
-      const int lane = lane_id();
+      const int e = EXTRA ? lane_id() : 8 * wave + (lane_id() & 7);   // the lane's entry
       const int32_t* src_ptr = p.sched;
       if (j < nsub) {
         const SubTile st = locate<EXTRA>(p, t0, j);
         if (st.count > 0)
-          src_ptr = (st.fp4 ? p.xidx : p.idx) + (int64_t)row * st.count + min(st.pos0 + lane, st.count - 1);
+          src_ptr = (st.fp4 ? p.xidx : p.idx) + (int64_t)row * st.count + min(st.pos0 + e, st.count - 1);
       }
-      copy4_to_lds_masked(src_ptr, __builtin_amdgcn_readfirstlane(lds_addr(idx_ring + slot * kIdxBytes)),
-                          0xFFFFFFFFull);
+      copy4_to_lds_masked(src_ptr,
+                          __builtin_amdgcn_readfirstlane(lds_addr(idx_ring + slot * kIdxBytes) + (EXTRA ? 0 : 32 * wave)),
+                          EXTRA ? 0xFFFFFFFFull : 0xFFull);
     };
 
     // ---- segment start: the first batch of the live-length scan, the first two index rows of
@@ -646,13 +667,16 @@ void sparse_decode_wide_kernel(DecodeParams p) {
       // The first three sub-tiles are gathered as soon as their index rows are in, while Q is
       // still arriving: the pipeline then starts one memory latency after the Q traffic instead
       // of two. The scan batch and idx(0 .. 2) have landed once at most the 32 Q loads issued
-      // after them are outstanding. A later segment first waits until every wave is done with the
+      // after them are outstanding; the barrier makes every wave's quarter of the shared index
+      // slots visible. It also keeps a later segment's gathers until every wave is done with the
       // previous segment's epilogue staging, which overlaps the raw slots.
       asm volatile("s_waitcnt vmcnt(32)" ::: "memory");
-      if (!first_seg) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 #pragma unroll
       for (int j = 0; j < 3; ++j) mk_first[j] = fp8_gather_first(j, nsub_all);
-      load_indices(3, 0);                        // the slots' entries are read (lgkmcnt waited)
+      // every wave has read slots 0 and 1 before any wave refills them
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      load_indices(3, 0);
       load_indices(4, 1);
     }
     if constexpr (FUSED) {
@@ -750,8 +774,13 @@ void sparse_decode_wide_kernel(DecodeParams p) {
       nsub = __builtin_amdgcn_readfirstlane(max(max(slots[0], slots[1]), max(slots[2], slots[3])) + 1);
       seg_parity ^= 1;
     }
-    const int split_base = p.split_ptr ? p.split_ptr[row] : 0;
-    const int nsplit = p.split_ptr ? p.split_ptr[row + 1] - split_base : 1;
+    // (the pointer is taken afresh here, so that its null test is not hoisted into a register
+    // kept through the pipeline)
+    typedef __attribute__((address_space(1))) const int32_t global_i32;
+    global_i32* split_ptr = (global_i32*)p.split_ptr;
+    asm volatile("" : "+s"(split_ptr));
+    const int split_base = split_ptr ? split_ptr[row] : 0;
+    const int nsplit = split_ptr ? split_ptr[row + 1] - split_base : 1;
     const int slot = first_seg ? slot_first : split_base;
 
     // Q and the first two index rows are resident before any further asynchronous copy of this
@@ -849,7 +878,8 @@ void sparse_decode_wide_kernel(DecodeParams p) {
     // 4 (kk / 2) + ((2 (kk % 2) + g) ^ tile_xor(r)), i.e. k_addr[kk % 8] + 256 (kk / 8).
     // PV step (ks, d) reads, for h = 0, 1, token row 16ks + 8((l/16)/2) + 4h + (l%16)/4 and logical
     // chunk 4d + 2((l/16)%2) + (l%4)/2 (8-byte half l%2), i.e. v_addr[4h + d%4] + 16 kTileStride ks
-    // + 256 (d / 4).
+    // + 256 (d / 4). The fp8 pipeline only reads its own dim blocks d = 4w .. 4w+3, and its v_addr
+    // already hold the + 256 w.
     uint32_t k_addr[8], v_addr[8];
     {
       const int lane = lane_id();
@@ -865,7 +895,8 @@ void sparse_decode_wide_kernel(DecodeParams p) {
         const int xr = tile_xor(rw);
 #pragma unroll
         for (int dd = 0; dd < 4; ++dd)
-          v_addr[4 * h + dd] = lds_addr(tiles + rw * kTileStride + 16 * (4 * dd + (c_lo ^ xr)) + 8 * (jj & 1));
+          v_addr[4 * h + dd] = lds_addr(tiles + rw * kTileStride + 16 * (4 * dd + (c_lo ^ xr)) + 8 * (jj & 1) +
+                                        (EXTRA ? 0 : 256 * wave));
       }
     }
     // Operand base of tile slot `sl` (a constant in the unrolled fp8 loop). Offsets into slots 0
@@ -882,9 +913,10 @@ void sparse_decode_wide_kernel(DecodeParams p) {
     //  raw_r    raw slot 0 address of the lane's first fp8 chunk (c0, token t); chunk c0 + cc at
     //           + 512 cc;  raw_s  the lane's two scale bytes (c0 / 2, token t);
     //  idx_r    index slot 0 entry of token t;  idx_v  its byte offset in a 32-entry index block;
+    //  idx_l    byte offset of the entry this lane loads into the shared ring (8 w + l, l < 8);
     //  g_base / g_zb   record byte 32 w + 16 hh (this lane's first copied chunk) of record 0 of
     //           the cache and of the zero record.
-    uint32_t dq_w[4], raw_r, raw_s, idx_r, idx_v;
+    uint32_t dq_w[4], raw_r, raw_s, idx_r, idx_v, idx_l;
     uint64_t g_base, g_zb;
     {
       const int lane = lane_id();
@@ -897,11 +929,16 @@ void sparse_decode_wide_kernel(DecodeParams p) {
       raw_s = lds_addr(raws + (32 * kSubTokens + t) * 16 + c0 / 2);
       idx_r = lds_addr(idx_ring + 4 * t);
       idx_v = 4 * t;
+      idx_l = 4 * (8 * wave + (lane & 7));
       g_base = (uint64_t)(uintptr_t)(p.kc + 32 * wave + 16 * hh);
       g_zb = (uint64_t)(uintptr_t)(g_zero.bytes + 32 * wave + 16 * hh);
       asm volatile("" : "+v"(dq_w[0]), "+v"(dq_w[1]), "+v"(dq_w[2]), "+v"(dq_w[3]), "+v"(raw_r),
-                   "+v"(raw_s), "+v"(idx_r), "+v"(idx_v), "+v"(g_base), "+v"(g_zb));
+                   "+v"(raw_s), "+v"(idx_r), "+v"(idx_v), "+v"(idx_l), "+v"(g_base), "+v"(g_zb));
     }
+    //  p_rd     P^T exchange buffer address of this lane's 16 bytes of head group 0, token half 0
+    //           (group g, half ks at + 1024 (2 g + ks)).
+    uint32_t p_rd = lds_addr(smem) + L::kOffP + 16 * lane_id();
+    asm volatile("" : "+v"(p_rd));
     // byte address of the segment row's index entries (the buffer base of the index loads)
     const uint64_t idx_row = (uint64_t)(uintptr_t)(p.idx + (int64_t)row * p.topk);
     auto slot_addr = [&](const uint32_t (&base)[8], int sl, uint32_t (&out)[8]) {
@@ -1085,8 +1122,10 @@ void sparse_decode_wide_kernel(DecodeParams p) {
 
       // ---- one iteration of the fp8-only pipeline, the same code for every s in [-4, nsub):
       // phase A runs the 32 QK^T MFMAs of sub-tile s+1 with the index load of s+6, the gather of
-      // s+4 and the dequantization of s+2 spread between them; phase B runs the 32 PV MFMAs of
-      // sub-tile s with the softmax of s+1 spread between them. Every step ends in a scheduling
+      // s+4 and half the dequantization of s+2 spread between them; phase B runs the 32 PV MFMAs
+      // of sub-tile s with the softmax of s+1 and the other half of the dequantization spread
+      // between them. The barrier at phase B's step 27 and one at the start of phase A order the
+      // tile, raw-slot and P^T exchange traffic across waves. Every step ends in a scheduling
       // barrier, so each piece stays next to its MFMA. Sub-tiles outside 0..nsub-1 take part with
       // an all-invalid mask: they gather from a valid dummy address, dequantize to zeros, get zero
       // probabilities and add nothing.
@@ -1097,11 +1136,14 @@ void sparse_decode_wide_kernel(DecodeParams p) {
         // + 64 (n % 16), h = 0, 1
         const uint32_t ka[2] = {slot_base(k_addr[0], r1), slot_base(k_addr[1], r1)};
         const uint32_t va[2] = {slot_base(v_addr[0], r0), slot_base(v_addr[4], r0)};
+        // V^T operand n (0..7): token half n / 4, this wave's dim block n % 4
         auto read_v = [&](int n) {
-          const uint32_t off = 16 * kTileStride * (n >> 4) + 64 * (n & 15);
+          const uint32_t off = 16 * kTileStride * (n >> 2) + 64 * (n & 3);
           return lds_v(va[0] + off, va[1] + off);
         };
-        bf16x8 vb[kRing];
+        // PV operands: V^T through a ring of three (operand n in vv[n % 3]), P^T of head group g
+        // for the first and second token half in p0[g], p1[g]
+        bf16x8 vv[3], p0[4], p1[4];
         f32x16 s_acc;
         // A operand of the extra k-step: lane l (token l%32, dims 8(l/32) ..) holds bf16 1.0 in
         // dim 1 if token l%32 of sub-tile s+1 is ignored (lanes 0..31 only)
@@ -1117,6 +1159,20 @@ void sparse_decode_wide_kernel(DecodeParams p) {
         uint32_t sc2 = 0;
         u32x4 rr0, rr1;
         bf16x8 dlo, dhi;
+        // step k (0..15) of that dequantization: raw chunk cc = k / 4 (in rr0, rr1, rr0, rr1),
+        // its first and second 8 values, then both bf16 chunks to the tile
+        auto dequant_step = [&](int k) {
+          const int cc = k >> 2, part = k & 3;
+          const uint32_t sb = (sc2 >> (8 * (cc >> 1))) & 0xFFu;
+          const u32x4& r = (cc & 1) ? rr1 : rr0;
+          if (part == 0) dlo = dequant_fp8_8(r[0], r[1], sb);
+          else if (part == 1) dhi = dequant_fp8_8(r[2], r[3], sb);
+          else if (part == 2) {
+            // bf16 chunks j = 2 cc (dlo) and 2 cc + 1 (dhi)
+            lds_write16_at(dqa[(2 * cc) & 3] + 64 * ((2 * cc) >> 2), __builtin_bit_cast(u32x4, dlo));
+            lds_write16_at(dqa[(2 * cc + 1) & 3] + 64 * ((2 * cc + 1) >> 2), __builtin_bit_cast(u32x4, dhi));
+          }
+        };
         // gather of s+4 (index slot r1 -> raw slot r1): tokens t < g_lim of the sub-tile are in
         // the index row (none past the live segment)
         const int g_pos0 = kUnitTokens * t0 + kSubTokens * (s + 4);   // fp8 sub-tile s+4
@@ -1127,13 +1183,20 @@ void sparse_decode_wide_kernel(DecodeParams p) {
         uint64_t gdat = 0;
 #pragma unroll
         for (int i = 0; i < 32; ++i) {
-          // operands are read kAhead MFMAs ahead, into phase B's first V operands at the end
+          // The P^T operands written at the end of the previous iteration (its last three LDS
+          // operations are the K reads that follow them) are visible to every wave after this
+          // barrier; the first P^T read is at step 27.
+          if (i == 0) asm volatile("s_waitcnt lgkmcnt(3)\n\ts_barrier" ::: "memory");
+          // operands are read kAhead MFMAs ahead, into phase B's first operands at the end
           if (i + kAhead < 32) {
             const int kk = i + kAhead;
             kb[kk % kRing] = lds_k(ka[kk & 1] + 64 * (kk >> 1));
           } else {
-            const int n = i + kAhead - 32;                  // phase B's first V operands
-            vb[n % kRing] = read_v(n);
+            // phase B's first operands: V^T 0 (step 27), P^T of the first token half of head
+            // groups 0..3 (steps 27..30), V^T 1 (step 31)
+            if (i == 27) vv[0] = read_v(0);
+            if (i < 31) p0[i - 27] = lds_k(p_rd + 2048 * (i - 27));
+            if (i == 31) vv[1] = read_v(1);
           }
           // operands are awaited in pairs: before an even step, the next step's operand too, so
           // that every other step needs no wait of its own
@@ -1189,49 +1252,51 @@ void sparse_decode_wide_kernel(DecodeParams p) {
             qflag = __builtin_bit_cast(bf16x8, u32x4{g0, 0u, 0u, 0u});
           }
           if (i == 26) {
-            // index load of sub-tile s+6 (positions 64 t0 + 32 (s+6) + t) into index slot r0 from a
-            // buffer that ends at the index row's end, or is empty past the live segment
+            // index load of sub-tile s+6 (positions 64 t0 + 32 (s+6) + 8 w + l, lanes l < 8) into
+            // this wave's quarter of the shared index slot r0, from a buffer that ends at the index
+            // row's end, or is empty past the live segment
             const int pos = kUnitTokens * t0 + kSubTokens * (s + 6);
             const int n_in = (s + 6 < nsub && p.topk > pos) ? p.topk - pos : 0;
             const uint64_t base = idx_row + (uint64_t)(4 * (int64_t)pos);
             const u32x4 rsrc = {(uint32_t)base, (uint32_t)(base >> 32) & 0xFFFFu, (uint32_t)(4 * n_in),
                                 0x00020000u};
-            buffer_copy4_to_lds(rsrc, idx_v, lds_addr(smem) + kOffIdx + (wave * kStages + r0) * kIdxBytes,
-                                0xFFFFFFFFull);
+            buffer_copy4_to_lds(rsrc, idx_l, lds_addr(smem) + kOffIdx + r0 * kIdxBytes + 32 * wave, 0xFFull);
           }
           // the second pair of raw chunks, once the first pair's values are converted
           if (i == 10) rr0 = *(lds_u32x4*)(uintptr_t)(draw + 1024);
           if (i == 14) rr1 = *(lds_u32x4*)(uintptr_t)(draw + 1536);
-          if (i >= 8 && i < 24) {
-            const int cc = (i - 8) >> 2, part = (i - 8) & 3;
-            const uint32_t sb = (sc2 >> (8 * (cc >> 1))) & 0xFFu;
-            const u32x4& r = (cc & 1) ? rr1 : rr0;
-            if (part == 0) dlo = dequant_fp8_8(r[0], r[1], sb);
-            else if (part == 1) dhi = dequant_fp8_8(r[2], r[3], sb);
-            else if (part == 2) {
-              // bf16 chunks j = 2 cc (dlo) and 2 cc + 1 (dhi)
-              lds_write16_at(dqa[(2 * cc) & 3] + 64 * ((2 * cc) >> 2), __builtin_bit_cast(u32x4, dlo));
-              lds_write16_at(dqa[(2 * cc + 1) & 3] + 64 * ((2 * cc + 1) >> 2), __builtin_bit_cast(u32x4, dhi));
-            }
-          }
+          // the first two of the four raw chunks here, the other two in phase B (whose LDS traffic
+          // is lighter), four steps each
+          if (i >= 8 && i < 16) dequant_step(i - 8);
           __builtin_amdgcn_sched_barrier(0);
         }
 
-        // phase B: PV of sub-tile s with the softmax of sub-tile s+1. The P^T operand of the first
-        // token half replaces pb_cur[0] (last read by PV step 15) as soon as it is built.
+        // phase B: PV of sub-tile s for this wave's 128 dims and all four head groups, with the
+        // softmax of sub-tile s+1 (this wave's heads). Step i accumulates block i % 16 = 4 b + g
+        // (dim block 4 w + b, head group g) over token half i / 16: V^T operand i / 4 with the
+        // P^T operand of group g. The P^T operands of sub-tile s+1 are written to the exchange
+        // buffer after the barrier at step 27, by which every wave has read those of sub-tile s.
         const uint32_t kb_next[2] = {slot_base(k_addr[0], r2), slot_base(k_addr[1], r2)};
         bf16x8 pb_new[2];
         SoftmaxTemps st;
 #pragma unroll
         for (int i = 0; i < 32; ++i) {
-          if (i + kAhead < 32) vb[(i + kAhead) % kRing] = read_v(i + kAhead);
-          if ((i & 1) == 0) asm volatile("" ::"v"(vb[(i + 1) % kRing]));
-          mfma_pv(oacc[i & 15], vb[i % kRing], pb_cur[i >> 4]);
+          if ((i + kAhead) % 4 == 0 && i + kAhead < 32) vv[((i + kAhead) / 4) % 3] = read_v((i + kAhead) / 4);
+          if (i >= 16 - kAhead && i < 20 - kAhead) p1[i - (16 - kAhead)] = lds_k(p_rd + 2048 * (i - (16 - kAhead)) + 1024);
+          // each new operand set is awaited in one wait
+          if (i == 0) asm volatile("" ::"v"(p0[0]), "v"(p0[1]), "v"(p0[2]), "v"(p0[3]), "v"(vv[0]));
+          if (i == 16) asm volatile("" ::"v"(p1[0]), "v"(p1[1]), "v"(p1[2]), "v"(p1[3]), "v"(vv[1]));
+          mfma_pv(oacc[i & 15], vv[(i / 4) % 3], i < 16 ? p0[i & 3] : p1[i & 3]);
           // the scores are read by VALU instructions next: 20 wait states after the last QK^T
           // MFMA (the PV MFMA above runs meanwhile)
           if (i == 0) asm volatile("s_nop 15\n\ts_nop 3" : "+v"(s_acc));
           if ((i & 1) == 0) softmax_step_fp8(st, i >> 1, s_acc, mk1 != 0, pb_new);   // steps 0..15
-          if (i == 26) pb_cur[0] = pb_new[0];
+          if (i >= 1 && i < 9) dequant_step(i + 7);
+          if (i == 29) {
+            // this wave's P^T operands of sub-tile s+1 (built at steps 26 and 28)
+            asm volatile("ds_write_b128 %0, %1\n\tds_write_b128 %0, %2 offset:1024"
+                         :: "v"(p_rd + 2048 * wave), "v"(pb_new[0]), "v"(pb_new[1]) : "memory");
+          }
           if (i == 32 - kAhead) {
             // Start of iteration s+1, while the last PV MFMAs (operands already read) still run:
             // every V read of this iteration is complete, idx(s+5) and the gather of s+3 (issued
@@ -1245,7 +1310,6 @@ void sparse_decode_wide_kernel(DecodeParams p) {
           }
           __builtin_amdgcn_sched_barrier(0);
         }
-        pb_cur[1] = pb_new[1];
       };
 
 
@@ -1259,9 +1323,10 @@ void sparse_decode_wide_kernel(DecodeParams p) {
         load_indices(0, 0);
         load_indices(1, 1);
         load_indices(2, 2);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
 #pragma unroll
         for (int j = 0; j < 3; ++j) mk_first[j] = fp8_gather_first(j, nsub);
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
         load_indices(3, 0);
         load_indices(4, 1);
       }
@@ -1288,6 +1353,10 @@ void sparse_decode_wide_kernel(DecodeParams p) {
             lds_write16(trow + 16 * ((2 * (c0 + cc) + 1) ^ sw), __builtin_bit_cast(u32x4, dequant_fp8_8(r[2], r[3], sb)));
           }
         }
+        // zero P^T operands for the PV of iteration -1, which runs on a tile slot no sub-tile of
+        // this pass has been written to
+        for (int o = 16 * (64 * wave + lane_id()); o < kPBytes; o += 16 * 64 * kWaves)
+          lds_write16(smem + L::kOffP + o, u32x4{});
         // tile 0 is complete and raw slot 0 free for the gather of sub-tile 3
         wait_and_barrier(0);
         mk0 = 0u;
@@ -1388,30 +1457,53 @@ void sparse_decode_wide_kernel(DecodeParams p) {
       m_ref_next = m_max;
     }
 
-    // ---- epilogue of this row segment. O^T block d: lane l holds head l%32 and dims
-    // 32d + 8(r/4) + 4(l/32) + r%4.
+    // ---- epilogue of this row segment. O^T block j holds head group hg(j) and dim block d(j):
+    // lane l has head 32 hg + l%32 and dims 32 d + 8(r/4) + 4(l/32) + r%4 in register r. The fp8
+    // pipeline splits PV by dims (hg = j % 4, d = 4 w + j / 4), the extra-cache variant by heads
+    // (hg = w, d = j). Every head group's probability sum comes from the wave that owns its heads.
     {
       const int lane = lane_id();
       const int g = lane >> 5;
       const int h = lane & 31;
       const int head = head_base + h;
       const bool final_out = nsplit == 1;
-      const float inv = l_sum > 0.0f ? 1.0f / l_sum : 0.0f;
+      auto blk_hg = [&](int j) { return EXTRA ? wave : (j & 3); };
+      auto blk_d = [&](int j) { return EXTRA ? j : 4 * wave + (j >> 2); };
+      float inv_g[4];
+      if constexpr (EXTRA) {
+        inv_g[0] = l_sum > 0.0f ? 1.0f / l_sum : 0.0f;
+      } else {
+        // every wave is past its last PV (the barrier that ended the pass), so the exchange
+        // buffer is free for the four head groups' sums
+        float* const lsums = reinterpret_cast<float*>(smem + L::kOffP);
+        if (g == 0) lsums[32 * wave + h] = l_sum;
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float l = lsums[32 * k + h];
+          inv_g[k] = l > 0.0f ? 1.0f / l : 0.0f;
+        }
+      }
+      auto inv_of = [&](int j) { return EXTRA ? inv_g[0] : inv_g[j & 3]; };
       if (FUSED && final_out) {
-        // Fused decode: the rotary pairs of the output (blocks 14 and 15: dims 448 + 2i, 449 + 2i)
-        // are rotated back by the row's angle and every head row is cast to an fp8 record (512
-        // e4m3 values, then 16 e8m0 scales, one per 32-dim block d: k = ceil(log2(amax / 448)),
-        // values rounded to nearest, ties to even), staged in LDS (kFusedRow bytes per head) and
-        // stored as whole 528-byte records.
-        char* const stage = smem + wave * kStageBytes;
+        // Fused decode: the rotary pairs of the output (dim blocks 14 and 15: dims 448 + 2i,
+        // 449 + 2i) are rotated back by the row's angle and every head row is cast to an fp8 record
+        // (512 e4m3 values, then 16 e8m0 scales, one per 32-dim block d: k = ceil(log2(amax /
+        // 448)), values rounded to nearest, ties to even), staged in LDS (head group hg's rows at
+        // hg * kStageBytes, kFusedRow bytes apart) and stored by the group's wave as whole 528-byte
+        // records.
         const float* cs = p.rope_cos + (int64_t)row * 32 + 2 * g;
         const float* sn = p.rope_sin + (int64_t)row * 32 + 2 * g;
+        // scale bytes: per 4-block word (extra-cache variant: words 0..3 of the wave's heads;
+        // fp8 pipeline: word w of head group 0..3)
         uint32_t kb[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int d = 0; d < 16; ++d) {
+        for (int j = 0; j < 16; ++j) {
+          const int hg = blk_hg(j), d = blk_d(j);
+          const float inv = inv_of(j);
           float y[16];
 #pragma unroll
-          for (int r = 0; r < 16; ++r) y[r] = oacc[d][r] * inv;
+          for (int r = 0; r < 16; ++r) y[r] = oacc[j][r] * inv;
           if (d >= 14) {
             // dims 32 d + 8 rb + 4 g + {0..3}: pairs 16 (d - 14) + 4 rb + 2 g + {0, 1}
 #pragma unroll
@@ -1431,22 +1523,28 @@ void sparse_decode_wide_kernel(DecodeParams p) {
           for (int r = 0; r < 16; ++r) a = fmaxf(a, __builtin_fabsf(y[r]));
           a = max_xor32(a);
           const int k = fp8_block_exponent(a);
+          const uint32_t rowa = lds_addr(smem + hg * kStageBytes + h * kFusedRow + 4 * g) + 32 * d;
 #pragma unroll
           for (int rb = 0; rb < 4; ++rb) {
             const uint32_t w = e4m3_codes4(y[4 * rb], y[4 * rb + 1], y[4 * rb + 2], y[4 * rb + 3], k);
-            *reinterpret_cast<__attribute__((address_space(3))) uint32_t*>(
-                lds_addr(stage + h * kFusedRow + 32 * d + 8 * rb + 4 * g)) = w;
+            *reinterpret_cast<__attribute__((address_space(3))) uint32_t*>(rowa + 8 * rb) = w;
           }
-          kb[d >> 2] |= (uint32_t)(k + 127) << (8 * (d & 3));
+          if (EXTRA) kb[j >> 2] |= (uint32_t)(k + 127) << (8 * (j & 3));
+          else kb[j & 3] |= (uint32_t)(k + 127) << (8 * (j >> 2));
           __builtin_amdgcn_sched_barrier(0);
         }
         if (g == 0) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
+          for (int i = 0; i < 4; ++i) {
+            // word i: head group hg, scale bytes 4 q .. 4 q + 3
+            const int hg = EXTRA ? wave : i, q = EXTRA ? i : wave;
             *reinterpret_cast<__attribute__((address_space(3))) uint32_t*>(
-                lds_addr(stage + h * kFusedRow + kHeadDim + 4 * i)) = kb[i];
+                lds_addr(smem + hg * kStageBytes + h * kFusedRow + kHeadDim + 4 * q)) = kb[i];
+          }
         }
-        // record rr, 16-byte chunk c (33 per record) from lane (33 rr + c) % 64
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        // this wave's head group: record rr, 16-byte chunk c (33 per record) from lane (33 rr + c) % 64
+        char* const stage = smem + wave * kStageBytes;
         for (int e = lane; e < 32 * (kFusedRow / 16); e += 64) {
           const int rr = e / (kFusedRow / 16), c = e % (kFusedRow / 16);
           if (head_base + rr < p.h_q) {
@@ -1457,23 +1555,25 @@ void sparse_decode_wide_kernel(DecodeParams p) {
         }
       } else if (final_out) {
         // Final rows in bf16, staged through LDS so that every store writes one head's 1 KB row:
-        // the wave's 32 rows go to its own kStageBytes (the tiles and the start of the raw slots,
-        // free after the pass); 8-byte unit u (dims 4u .. 4u+3) of head h at h * kStageRow + 8u.
-        // Every LDS address is a per-lane base plus an immediate.
-        char* const stage = smem + wave * kStageBytes;
-        const uint32_t wbase = lds_addr(stage + h * kStageRow + 8 * g);
+        // head 32 hg + h at hg * kStageBytes + h * kStageRow (the tiles and the start of the raw
+        // slots, free after the pass); 8-byte unit u (dims 4u .. 4u+3) at + 8u. Each wave writes
+        // its blocks, then stores the 32 rows of its own head group.
+        const uint32_t wbase = lds_addr(smem + h * kStageRow + 8 * g);
 #pragma unroll
-        for (int d = 0; d < 16; ++d) {
+        for (int j = 0; j < 16; ++j) {
+          const uint32_t jbase = wbase + blk_hg(j) * kStageBytes + 64 * blk_d(j);
+          const float inv = inv_of(j);
 #pragma unroll
           for (int jb = 0; jb < 4; ++jb) {
             bf16x4 o;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) o[i] = (__bf16)(oacc[d][4 * jb + i] * inv);
-            *reinterpret_cast<lds_bf16x4_w*>(wbase + 64 * d + 16 * jb) = o;
+            for (int i = 0; i < 4; ++i) o[i] = (__bf16)(oacc[j][4 * jb + i] * inv);
+            *reinterpret_cast<lds_bf16x4_w*>(jbase + 16 * jb) = o;
           }
         }
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
         // row r: lane l moves dims 8l .. 8l+7 (units 2l, 2l+1), stored from a uniform row address
-        const uint32_t rbase = lds_addr(stage + 16 * lane);
+        const uint32_t rbase = lds_addr(smem + wave * kStageBytes + 16 * lane);
         char* const orow = reinterpret_cast<char*>(p.out) + ((int64_t)row * p.h_q + head_base) * (2 * kHeadDim);
         for (int r = 0; r < 32 && head_base + r < p.h_q; ++r) {
           const bf16x4 lo = *reinterpret_cast<const lds_bf16x4_w*>(rbase + r * kStageRow);
@@ -1481,16 +1581,20 @@ void sparse_decode_wide_kernel(DecodeParams p) {
           *reinterpret_cast<bf16x8*>(orow + r * (2 * kHeadDim) + 16 * lane) =
               __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         }
-      } else if (head < p.h_q) {
+      } else {
 #pragma unroll
-        for (int d = 0; d < 16; ++d) {
+        for (int j = 0; j < 16; ++j) {
+          const int head_j = blockIdx.y * kGroupHeads + 32 * blk_hg(j) + h;
+          const float inv = inv_of(j);
+          if (head_j < p.h_q) {
 #pragma unroll
-          for (int jb = 0; jb < 4; ++jb) {
-            const int dim = 32 * d + 8 * jb + 4 * g;
-            f32x4 o;
+            for (int jb = 0; jb < 4; ++jb) {
+              const int dim = 32 * blk_d(j) + 8 * jb + 4 * g;
+              f32x4 o;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) o[i] = oacc[d][4 * jb + i] * inv;
-            *reinterpret_cast<f32x4*>(static_cast<float*>(p.part_o) + ((int64_t)slot * p.h_q + head) * kHeadDim + dim) = o;
+              for (int i = 0; i < 4; ++i) o[i] = oacc[j][4 * jb + i] * inv;
+              *reinterpret_cast<f32x4*>(static_cast<float*>(p.part_o) + ((int64_t)slot * p.h_q + head_j) * kHeadDim + dim) = o;
+            }
           }
           __builtin_amdgcn_sched_barrier(0);
         }

@@ -1194,6 +1194,7 @@ void sparse_decode_wide_kernel(DecodeParams p) {
           } else {
             // phase B's first operands: V^T 0 (step 27), P^T of the first token half of head
             // groups 0..3 (steps 27..30), V^T 1 (step 31)
+            static_assert(kAhead == 5, "the reads below cover steps 32 - kAhead .. 31");
             if (i == 27) vv[0] = read_v(0);
             if (i < 31) p0[i - 27] = lds_k(p_rd + 2048 * (i - 27));
             if (i == 31) vv[1] = read_v(1);
@@ -1227,18 +1228,19 @@ void sparse_decode_wide_kernel(DecodeParams p) {
             const uint64_t a = g_base + (uint64_t)(int64_t)gv * kFp8Rec;
             gdat = valid ? a : g_zb;                         // chunk 2(w + 4i) + hh at +128 i
           }
-          // gather copies at steps 4..8: 4 chunk pairs (wave w moves chunks 2(w + 4c) + hh of all 32
-          // tokens) and the scale chunks of tokens 8w .. 8w+7 (lanes of the first half: the
-          // record's byte 512 is 512 - 32 w past gdat there)
-          if (i >= 4 && i < 8) {
-            const int c = i - 4;
+          // gather copies at steps 4, 9, 14, 19 and 24 (spread out, so that the address work of
+          // one 64-address copy is done before the next is issued): 4 chunk pairs (wave w moves
+          // chunks 2(w + 4c) + hh of all 32 tokens) and the scale chunks of tokens 8w .. 8w+7
+          // (lanes of the first half: the record's byte 512 is 512 - 32 w past gdat there)
+          if (i >= 4 && i < 24 && (i - 4) % 5 == 0) {
+            const int c = (i - 4) / 5;
             const uint32_t dst = __builtin_amdgcn_readfirstlane(graw + 1024 * (wave + 4 * c));
             const void* gp = (const void*)(uintptr_t)gdat;
             if (c == 0) copy16_to_lds_off<0>(gp, dst);
             else if (c == 1) copy16_to_lds_off<128>(gp, dst);
             else if (c == 2) copy16_to_lds_off<256>(gp, dst);
             else copy16_to_lds_off<384>(gp, dst);
-          } else if (i == 8) {
+          } else if (i == 24) {
             copy16_to_lds_masked((const void*)(uintptr_t)(gdat + (uint64_t)(512 - 32 * wave)),
                                  __builtin_amdgcn_readfirstlane(graw + 32 * 512), scale_lanes_fp8);
           }

@@ -24,7 +24,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmla.so")
-SOURCES = ["mla_decode.hip", "mla_decode_wide.hip", "mla_sched.hip", "mla_combine.hip", "mla_aux.hip",
+SOURCES = ["mla_decode.hip", "mla_decode_wide.hip", "mla_decode_h64.hip", "mla_sched.hip", "mla_combine.hip", "mla_aux.hip",
            "mla_noalloc.hip", "mla_quant.hip", "mla_api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -37,7 +37,8 @@ FLAGS = [
 
 
 # source -> kernel-name fragment whose assembly is checked by asm_check
-ASM_CHECKED = {"mla_decode_wide.hip": "sparse_decode_wide_kernel"}
+ASM_CHECKED = {"mla_decode_wide.hip": "sparse_decode_wide_kernel",
+               "mla_decode_h64.hip": "sparse_decode_h64_kernel"}
 
 
 class SpillError(RuntimeError):

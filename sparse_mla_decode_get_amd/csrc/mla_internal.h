@@ -79,6 +79,9 @@ int sparse_decode(const DecodeCall& c, const WorkspaceSource& ws);
 int launch_sparse_decode(const DecodeParams& p, int parts, int groups, int nw, hipStream_t stream);
 // 128-head groups, four waves of 32 heads each (mla_decode_wide.hip).
 int launch_sparse_decode_wide(const DecodeParams& p, int parts, int groups, hipStream_t stream);
+// 64-head groups of fp8 records only (no extra cache), four waves of 16 heads each
+// (mla_decode_h64.hip); its partials are bf16, like those of launch_sparse_decode.
+int launch_sparse_decode_h64(const DecodeParams& p, int parts, int groups, hipStream_t stream);
 int launch_metadata(int rows, int tiles, int parts, int32_t* sched, int32_t* split_ptr,
                     hipStream_t stream);
 // Merge of fp32 partials (mla_combine, and the 128-head decode's workspace) or of the 64-head

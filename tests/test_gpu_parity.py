@@ -353,3 +353,66 @@ def test_decode_replays_from_a_captured_graph(h_q):
         assert torch.equal(lse, eager_lse), f"replay {k}: lse differs from the eager decode"
     ref_out, ref_lse = _oracle(w)
     check_rows(out, lse, ref_out, ref_lse, "graph")
+
+
+# ------------------------------------------------ the single-stream 64-head kernel (mla_decode_h64)
+# h_q <= 64 without an extra cache runs in that kernel when the parts average at least 12 sub-tiles
+# of 32 tokens (2 * rows * units / parts >= 12); the cases below are sized for it, while the
+# default schedules of the small cases above run the two-half kernel (mla_decode.hip).
+
+def _stream_parts(spec, per_part):
+    """A part count that gives `per_part` sub-tiles per part (at least 12)."""
+    units = -(-spec.topk // 64)
+    parts = max(1, 2 * spec.rows * units // per_part)
+    assert 2 * spec.rows * units >= 12 * parts
+    return parts
+
+
+@pytest.mark.parametrize("spec,per_part", [
+    (Spec("stream_h64_whole_rows", 2, 2, 64, 1024, 4096, neg="tail10"), 32),
+    (Spec("stream_h64_split", 2, 2, 64, 1024, 4096, values="spread"), 16),
+    (Spec("stream_h40_multi_segment", 3, 2, 40, 700, 4096, neg="frac5"), 14),
+    (Spec("stream_h16", 2, 1, 16, 2048, 8192), 64),
+    (Spec("stream_h16_split", 2, 1, 16, 2048, 8192, neg="tail10"), 24),
+    (Spec("stream_h64_ragged_topk", 1, 3, 64, 1000, 8192, neg="frac5"), 32),
+], ids=lambda x: x.name if isinstance(x, Spec) else str(x))
+def test_decode_single_stream_64_head_kernel(spec, per_part):
+    w = make_workload(spec, seed=41)
+    out, lse, md = _decode(w, num_parts=_stream_parts(spec, per_part))
+    ref_out, ref_lse = _oracle(w)
+    check_rows(out, lse, ref_out, ref_lse, spec.name)
+
+
+@pytest.mark.parametrize("per_part", [32, 16])
+def test_stream_64_head_trailing_ignored_subtiles(per_part):
+    """As test_decode_trailing_ignored_subtiles, for the single-stream 64-head kernel: rows whose
+    selections end in runs of -1 of every length relative to the sub-tile, a fully ignored sub-tile
+    inside the live part, whole rows with no valid entry."""
+    spec = Spec("trailing64", 4, 2, 64, 1024, 4096)
+    w = make_workload(spec, seed=33)
+    idx = w["indices"].reshape(8, 1024)
+    for r, n_live in enumerate([0, 1, 31, 32, 33, 95, 500, 1024]):
+        idx[r, n_live:] = -1
+    idx[6, 64:96] = -1
+    idx[7, 1023] = -1
+    out, lse, md = _decode(w, num_parts=_stream_parts(spec, per_part))
+    ref_out, ref_lse = _oracle(w)
+    check_rows(out, lse, ref_out, ref_lse, f"trailing64/{per_part}")
+    assert torch.all(lse[0, 0] == -math.inf)
+    assert torch.all(out[0, 0] == 0)
+
+
+def test_stream_64_head_full_size_mid_workload():
+    """The mid workload (batch 32, h_q 64, topk 2048) at 64 parts, which runs the single-stream
+    kernel with two parts per row: every row against the oracle."""
+    w = make_workload(1)
+    spec = w["spec"]
+    out, lse, md = _decode(w, num_parts=64)
+    assert md.workspace is not None
+    o = out.reshape(spec.rows, spec.h_q, 512)
+    l = lse.reshape(spec.rows, spec.h_q)
+    for r0 in range(0, spec.rows, 16):
+        rows = list(range(r0, min(spec.rows, r0 + 16)))
+        ref_out, ref_lse = oracle_decode_rows(w["q_bits"], w["k_cache"], w["indices"],
+                                              w["softmax_scale"], rows)
+        check_rows(o[rows], l[rows], ref_out, ref_lse, f"mid/64 parts rows {rows[0]}..{rows[-1]}")

@@ -174,3 +174,35 @@ def test_score_growth_reaches_the_rescale_paths(name, h_q, extra, mode):
                                    d.get("extra_k_cache"), d.get("extra_indices"))
     torch.cuda.synchronize()
     check_rows(out2, lse2, ref_out, ref_lse, name + "/split")
+
+
+STREAM_CASES = [
+    ("h16_fp8_extreme_stream", 16, "extreme"),
+    ("h64_fp8_extreme_stream", 64, "extreme"),
+    ("h64_fp8_moderate_stream", 64, "moderate"),
+]
+
+
+@pytest.mark.parametrize("name,h_q,mode", STREAM_CASES, ids=[c[0] for c in STREAM_CASES])
+def test_score_growth_single_stream_64_head_kernel(name, h_q, mode):
+    """The single-stream 64-head kernel (fp8 only, parts of at least 12 sub-tiles) takes
+    probabilities against each head's first live sub-tile like the 128-head kernel: "extreme" rows
+    grow by more than 64 log2 units past it, which forces the second pass."""
+    spec = Spec(name, 4, 1, h_q, 1024, 8192)
+    w = _controlled(spec, seed=71 + h_q, mode=mode)
+    for r in range(spec.rows):
+        s, sub = _scores_log2(w, r)
+        first = sub == sub.min()
+        growth = s.max(axis=1) - s[:, first].max(axis=1)
+        if mode == "extreme":
+            assert growth.max() > 64, f"{name} row {r}: growth {growth.max():.1f} <= 64"
+        else:
+            assert growth.max() > 8, f"{name} row {r}: growth {growth.max():.1f} <= 8"
+    d = to_dev(w)
+    ref_out, ref_lse = oracle_decode(w["q_bits"], w["k_cache"], w["indices"], w["softmax_scale"])
+    # one part per row (32 sub-tiles), then two (16 sub-tiles each)
+    for parts in (spec.rows, 2 * spec.rows):
+        md = mla.get_metadata(spec.batch, spec.seq_len_q, h_q, spec.topk, 0, num_parts=parts)
+        out, lse = mla.sparse_decode(d["q"], d["k_cache"], d["indices"], w["softmax_scale"], md)
+        torch.cuda.synchronize()
+        check_rows(out, lse, ref_out, ref_lse, f"{name}/{parts} parts")

@@ -101,6 +101,8 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // Bytes per partial output value: the 64-head kernel writes bf16 partials (the merge takes them back
 // to fp32), the 128-head kernel fp32 ones (its registers leave no room for the conversion).
+// partials are bf16, except the fused 128-head decode's (fp32); the workspace is sized for the
+// larger, so that one workspace serves both entry points
 size_t partial_elem_bytes(int h_q) { return wide_for(h_q) ? sizeof(float) : sizeof(uint16_t); }
 
 size_t split_workspace_bytes(int batch, int seq_len_q, int h_q, int num_parts_used) {
@@ -204,12 +206,10 @@ int sparse_decode(const DecodeCall& c, const WorkspaceSource& ws) {
                              c.rope_cos, c.rope_sin, p.out_fp8, c.lse, s) != 0)
       return MLA_ERR_HIP;
   } else if (split) {
-    const int merged = wide_for(h_q)
-        ? launch_combine(static_cast<const float*>(part_o), part_lse, c.split_ptr, rows, h_q, p.out,
-                         c.lse, true, s)
-        : launch_combine_bf16(static_cast<const uint16_t*>(part_o), part_lse, c.split_ptr, rows,
-                              h_q, p.out, c.lse, s);
-    if (merged != 0) return MLA_ERR_HIP;
+    // every decode kernel writes bf16 partials for the plain decode
+    if (launch_combine_bf16(static_cast<const uint16_t*>(part_o), part_lse, c.split_ptr, rows, h_q,
+                            p.out, c.lse, s) != 0)
+      return MLA_ERR_HIP;
   }
   return MLA_OK;
 }

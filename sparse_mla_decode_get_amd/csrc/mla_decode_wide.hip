@@ -1584,18 +1584,29 @@ void sparse_decode_wide_kernel(DecodeParams p) {
               __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         }
       } else {
+        // the normalised partial of this split: bf16 for the merge of the plain decode (its
+        // rounding, 2^-9 relative, is far inside the output tolerance, and it halves the partial
+        // traffic), fp32 for the fused decode's merge, which encodes fp8 records from it
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
           const int head_j = blockIdx.y * kGroupHeads + 32 * blk_hg(j) + h;
           const float inv = inv_of(j);
           if (head_j < p.h_q) {
+            const int64_t base = ((int64_t)slot * p.h_q + head_j) * kHeadDim;
 #pragma unroll
             for (int jb = 0; jb < 4; ++jb) {
               const int dim = 32 * blk_d(j) + 8 * jb + 4 * g;
-              f32x4 o;
+              if constexpr (FUSED) {
+                f32x4 o;
 #pragma unroll
-              for (int i = 0; i < 4; ++i) o[i] = oacc[j][4 * jb + i] * inv;
-              *reinterpret_cast<f32x4*>(static_cast<float*>(p.part_o) + ((int64_t)slot * p.h_q + head_j) * kHeadDim + dim) = o;
+                for (int i = 0; i < 4; ++i) o[i] = oacc[j][4 * jb + i] * inv;
+                *reinterpret_cast<f32x4*>(static_cast<float*>(p.part_o) + base + dim) = o;
+              } else {
+                bf16x4 o;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) o[i] = (__bf16)(oacc[j][4 * jb + i] * inv);
+                *reinterpret_cast<bf16x4*>(static_cast<uint16_t*>(p.part_o) + base + dim) = o;
+              }
             }
           }
           __builtin_amdgcn_sched_barrier(0);

@@ -20,8 +20,8 @@ struct DecodeParams {
   const int32_t* split_ptr;  // [rows + 1]; null with prefill_parts > 0 (no row is split)
   int prefill_parts;         // > 0: no metadata; part b takes whole rows, prefill_q of them plus
   int prefill_q, prefill_r;  // one for b < prefill_r (rows = prefill_q * parts + prefill_r)
-  void* part_o;              // workspace partial outputs [slots][h_q][512]: fp32 from the 128-head
-                             // kernel, bf16 from the 64-head kernel
+  void* part_o;              // workspace partial outputs [slots][h_q][512]: bf16, except fp32 from
+                             // the fused 128-head decode
   float* part_lse;           // workspace partial lse [slots][h_q]
   uint16_t* out;             // bf16 [rows][h_q][512]
   float* lse;                // [rows][h_q]

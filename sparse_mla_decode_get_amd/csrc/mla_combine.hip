@@ -8,26 +8,30 @@
 
 namespace mla {
 
-constexpr int kCombineThreads = 128;   // 4 dims per thread
+constexpr int kCombineThreads = 128;   // the fused merge: 4 dims per thread
 
-// Four dims of one partial row as fp32: from fp32 partials (mla_combine's input) or from the bf16
-// partials the decode kernels write to their workspace.
-__device__ __forceinline__ f32x4 load4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
-__device__ __forceinline__ f32x4 load4(const uint16_t* p) {
-  const u32x2 w = *reinterpret_cast<const u32x2*>(p);
-  f32x4 r;
-  r[0] = __builtin_bit_cast(float, w[0] << 16);
-  r[1] = __builtin_bit_cast(float, w[0] & 0xFFFF0000u);
-  r[2] = __builtin_bit_cast(float, w[1] << 16);
-  r[3] = __builtin_bit_cast(float, w[1] & 0xFFFF0000u);
-  return r;
-}
+// One 16-byte load of a partial row per split and thread: 4 dims of fp32 partials (mla_combine's
+// input and the fused decode's workspace) or 8 dims of the bf16 partials the plain decode kernels
+// write, so that each load instruction moves as many bytes for either type.
+template <typename PT>
+struct PartialLoad {
+  static constexpr int kDims = 16 / (int)sizeof(PT);
+  static constexpr int kThreads = kHeadDim / kDims;
+  __device__ static float dim(const u32x4& w, int k) {
+    // the element is copied out first: bit-casting the vector element itself reads element 0
+    const uint32_t e = w[sizeof(PT) == 4 ? k : k >> 1];
+    if constexpr (sizeof(PT) == 4) return __builtin_bit_cast(float, e);
+    else return __builtin_bit_cast(float, (k & 1) ? (e & 0xFFFF0000u) : (e << 16));
+  }
+};
 
 template <typename PT>
-__global__ __launch_bounds__(kCombineThreads) void combine_kernel(
+__global__ __launch_bounds__(PartialLoad<PT>::kThreads) void combine_kernel(
     const PT* __restrict__ partial, const float* __restrict__ partial_lse,
     const int32_t* __restrict__ split_ptr, int h_q, uint16_t* __restrict__ out,
     float* __restrict__ lse, int skip_single) {
+  using PL = PartialLoad<PT>;
+  constexpr int kDims = PL::kDims;
   const int row = blockIdx.x;
   const int head = blockIdx.y;
   const int a = split_ptr[row];
@@ -35,7 +39,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
   if (skip_single && n == 1) return;      // written directly by the decode kernel
   const float ninf = -__builtin_inff();
   const float* lse_col = partial_lse + (int64_t)a * h_q + head;
-  const int dim = 4 * threadIdx.x;
+  const int dim = kDims * threadIdx.x;
   const PT* o_col = partial + ((int64_t)a * h_q + head) * kHeadDim + dim;
   // One pass over the splits, kBatch at a time, with every lse and partial load of a batch issued
   // before any is used (one memory round trip per batch, none waiting on an earlier maximum). The
@@ -43,23 +47,24 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
   // wsum = sum_i exp(lse_i - m), acc = sum_i exp(lse_i - m) o_i.
   constexpr int kBatch = 8;
   float m = ninf;
-  f32x4 acc = f32x4{};
+  float acc[kDims] = {};
   float wsum = 0.0f;
   for (int i0 = 0; i0 < n; i0 += kBatch) {
     float li[kBatch];
-    f32x4 o[kBatch];
+    u32x4 o[kBatch];
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       const bool in = i0 + u < n;
       li[u] = in ? lse_col[(int64_t)(i0 + u) * h_q] : ninf;
-      o[u] = in ? load4(o_col + (int64_t)(i0 + u) * h_q * kHeadDim) : f32x4{};
+      o[u] = in ? *reinterpret_cast<const u32x4*>(o_col + (int64_t)(i0 + u) * h_q * kHeadDim) : u32x4{};
     }
     float mb = m;
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) mb = fmaxf(mb, li[u]);
     if (mb == ninf) continue;                // no live split so far
     const float sc = __expf(m - mb);         // 0 while m = -inf, when acc and wsum are still 0
-    acc *= sc;
+#pragma unroll
+    for (int k = 0; k < kDims; ++k) acc[k] *= sc;
     wsum *= sc;
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
@@ -67,15 +72,24 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
       if (li[u] == ninf) continue;
       const float w = __expf(li[u] - mb);
       wsum += w;
-      acc += w * o[u];
+#pragma unroll
+      for (int k = 0; k < kDims; ++k) acc[k] += w * PL::dim(o[u], k);
     }
     m = mb;
   }
   const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
-  bf16x4 r;
+  uint16_t* const orow = out + ((int64_t)row * h_q + head) * kHeadDim + dim;
+  if constexpr (kDims == 4) {
+    bf16x4 r;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) r[i] = (__bf16)(acc[i] * inv);
-  *reinterpret_cast<bf16x4*>(out + ((int64_t)row * h_q + head) * kHeadDim + dim) = r;
+    for (int i = 0; i < 4; ++i) r[i] = (__bf16)(acc[i] * inv);
+    *reinterpret_cast<bf16x4*>(orow) = r;
+  } else {
+    bf16x8 r;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r[i] = (__bf16)(acc[i] * inv);
+    *reinterpret_cast<bf16x8*>(orow) = r;
+  }
   if (threadIdx.x == 0) lse[(int64_t)row * h_q + head] = wsum > 0.0f ? m + __logf(wsum) : ninf;
 }
 
@@ -101,7 +115,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_fused_kernel(
   for (int i = 0; i < n; ++i) {            // two passes are not needed: rescale as the max grows
     const float li = lse_col[(int64_t)i * h_q];
     if (li == ninf) continue;
-    const f32x4 o = load4(o_col + (int64_t)i * h_q * kHeadDim);
+    const f32x4 o = *reinterpret_cast<const f32x4*>(o_col + (int64_t)i * h_q * kHeadDim);
     const float mn = fmaxf(m, li);
     const float sc = __expf(m - mn);
     const float w = __expf(li - mn);
@@ -150,14 +164,14 @@ int launch_combine_fused(const float* partial, const float* partial_lse, const i
 int launch_combine(const float* partial, const float* partial_lse, const int32_t* split_ptr,
                    int rows, int h_q, uint16_t* out, float* lse, bool skip_single,
                    hipStream_t stream) {
-  hipLaunchKernelGGL(combine_kernel<float>, dim3(rows, h_q), dim3(kCombineThreads), 0, stream,
+  hipLaunchKernelGGL(combine_kernel<float>, dim3(rows, h_q), dim3(PartialLoad<float>::kThreads), 0, stream,
                      partial, partial_lse, split_ptr, h_q, out, lse, skip_single ? 1 : 0);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 int launch_combine_bf16(const uint16_t* partial, const float* partial_lse, const int32_t* split_ptr,
                         int rows, int h_q, uint16_t* out, float* lse, hipStream_t stream) {
-  hipLaunchKernelGGL(combine_kernel<uint16_t>, dim3(rows, h_q), dim3(kCombineThreads), 0, stream,
+  hipLaunchKernelGGL(combine_kernel<uint16_t>, dim3(rows, h_q), dim3(PartialLoad<uint16_t>::kThreads), 0, stream,
                      partial, partial_lse, split_ptr, h_q, out, lse, 1);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }

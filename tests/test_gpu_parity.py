@@ -358,11 +358,12 @@ def test_decode_replays_from_a_captured_graph(h_q):
 # ------------------------------------------------ the single-stream 64-head kernel (mla_decode_h64)
 # h_q <= 64 without an extra cache runs in that kernel when the parts average at least 12 sub-tiles
 # of 32 tokens (2 * rows * units / parts >= 12); the cases below are sized for it, while the
-# default schedules of the small cases above run the two-half kernel (mla_decode.hip).
+# default schedules of the small cases above run the two-half kernel (mla_decode.hip), as does
+# every decode with an extra cache.
 
 def _stream_parts(spec, per_part):
-    """A part count that gives `per_part` sub-tiles per part (at least 12)."""
-    units = -(-spec.topk // 64)
+    """A part count that gives `per_part` sub-tiles per part (at least 12), units of both caches."""
+    units = -(-spec.topk // 64) + -(-spec.extra_topk // 64)
     parts = max(1, 2 * spec.rows * units // per_part)
     assert 2 * spec.rows * units >= 12 * parts
     return parts
@@ -398,6 +399,52 @@ def test_stream_64_head_trailing_ignored_subtiles(per_part):
     out, lse, md = _decode(w, num_parts=_stream_parts(spec, per_part))
     ref_out, ref_lse = _oracle(w)
     check_rows(out, lse, ref_out, ref_lse, f"trailing64/{per_part}")
+    assert torch.all(lse[0, 0] == -math.inf)
+    assert torch.all(out[0, 0] == 0)
+
+
+@pytest.mark.parametrize("spec,per_part", [
+    # parts cut rows inside either cache's sub-tiles and across the boundary between them
+    (Spec("long_parts_mixed_split", 2, 2, 64, 1000, 4096, extra_topk=300, extra_tokens_per_seq=2048,
+          neg="frac5"), 14),
+    (Spec("long_parts_mixed_whole_rows", 2, 1, 64, 2048, 8192, extra_topk=512,
+          extra_tokens_per_seq=2048), 80),
+    # fp8 list ending 13 tokens into its last unit, so its last sub-tile is empty before the
+    # fp4 sub-tiles start
+    (Spec("long_parts_h16_mixed_ragged", 1, 3, 16, 333, 4096, extra_topk=129, extra_tokens_per_seq=1024,
+          values="spread"), 12),
+    (Spec("long_parts_fp4_only", 2, 2, 64, 0, 64, extra_topk=800, extra_tokens_per_seq=4096,
+          neg="tail10"), 13),
+    (Spec("long_parts_h40_mixed", 3, 1, 40, 700, 4096, extra_topk=200, extra_tokens_per_seq=1024), 16),
+], ids=lambda x: x.name if isinstance(x, Spec) else str(x))
+def test_decode_64_head_extra_cache_long_parts(spec, per_part):
+    """Extra-cache decodes (two-half kernel) with parts of 12 and more sub-tiles, whose segments
+    start inside either cache's sub-tiles or cross from the one to the other."""
+    w = make_workload(spec, seed=43)
+    out, lse, md = _decode(w, num_parts=_stream_parts(spec, per_part))
+    ref_out, ref_lse = _oracle(w)
+    check_rows(out, lse, ref_out, ref_lse, spec.name)
+
+
+@pytest.mark.parametrize("per_part", [24, 12])
+def test_64_head_ignored_runs_in_either_cache(per_part):
+    """Extra-cache decodes with rows that have no valid entry in either list, in only one of them,
+    and runs of -1 ending each list part-way through a sub-tile."""
+    spec = Spec("ignored_mixed", 5, 1, 64, 512, 4096, extra_topk=256, extra_tokens_per_seq=1024)
+    w = make_workload(spec, seed=37)
+    idx = w["indices"].reshape(5, 512)
+    xidx = w["extra_indices"].reshape(5, 256)
+    idx[0] = -1
+    xidx[0] = -1
+    idx[1] = -1
+    xidx[2] = -1
+    idx[3, 100:] = -1
+    xidx[3, 33:] = -1
+    idx[4, 200:480] = -1
+    xidx[4, :64] = -1
+    out, lse, md = _decode(w, num_parts=_stream_parts(spec, per_part))
+    ref_out, ref_lse = _oracle(w)
+    check_rows(out, lse, ref_out, ref_lse, f"ignored_mixed/{per_part}")
     assert torch.all(lse[0, 0] == -math.inf)
     assert torch.all(out[0, 0] == 0)
 

@@ -191,9 +191,10 @@ void sparse_decode_h64_kernel(DecodeParams p) {
   const int head_base = group_base + 16 * wave;                 // this wave's first QK^T head
   const uint64_t scale_lanes = 0xFFull << (8 * wave);           // scale chunks of tokens 8w..8w+7
 
-  // iteration -1 runs PV on a tile slot no sub-tile has been written to, with zero
-  // probabilities: zeros keep those products finite
-  for (int o = threadIdx.x * 16; o < kStages * kTileBytes; o += 64 * kWaves * 16)
+  // iteration -1 runs PV on tile slot 2, which no sub-tile has been written to, with zero
+  // probabilities: zeros keep those products finite (slots 0 and 1 are written before they are
+  // read)
+  for (int o = 2 * kTileBytes + threadIdx.x * 16; o < 3 * kTileBytes; o += 64 * kWaves * 16)
     *reinterpret_cast<u32x4*>(tiles + o) = u32x4{};
   __syncthreads();
 

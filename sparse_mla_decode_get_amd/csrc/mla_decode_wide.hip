@@ -547,10 +547,11 @@ void sparse_decode_wide_kernel(DecodeParams p) {
   const uint64_t scale_lanes_fp4 = scale_lanes_fp8 | (scale_lanes_fp8 << 32);
 
   if constexpr (!EXTRA) {
-    // The fp8 pipeline's first full iteration (-1) runs PV on a tile slot no sub-tile has been
-    // written to yet, with zero probabilities: zeros keep those products finite. Later segments
-    // find finite data there (earlier sub-tiles, or the staged bf16 output).
-    for (int o = threadIdx.x * 16; o < kStages * kTileBytes; o += 64 * kWaves * 16)
+    // The fp8 pipeline's first full iteration (-1) runs PV on tile slot 2, which no sub-tile has
+    // been written to yet, with zero probabilities: zeros keep those products finite (slots 0 and
+    // 1 are written before they are read). Later segments find finite data there (earlier
+    // sub-tiles, or the staged bf16 output).
+    for (int o = 2 * kTileBytes + threadIdx.x * 16; o < 3 * kTileBytes; o += 64 * kWaves * 16)
       lds_write16(tiles + o, u32x4{});
     __syncthreads();
   }

@@ -23,9 +23,10 @@ shorter than the host's launch time (the mid and mixed workloads, or any run und
 measure the GPU rather than the launch rate.
 
   python bench.py [--gpus 1] [--steps 2000] [--warmup 300] [--prewarm-s 0.3] [--config 2]
-                  [--graph] [--no-cpu-baseline]
+                  [--batch N] [--parts N] [--graph] [--no-cpu-baseline]
 """
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -227,6 +228,11 @@ def main():
     ap.add_argument("--prewarm-s", type=float, default=0.3,
                     help="untimed steps for this many seconds before the warm-up steps")
     ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--batch", type=int, default=0,
+                    help="run the --config workload's per-row recipe at this batch instead (0: the "
+                         "config's own); fewer rows leave CUs idle, for occupancy and clock studies")
+    ap.add_argument("--parts", type=int, default=0,
+                    help="decode parts of the schedule (0: the library's default for the shape)")
     ap.add_argument("--sets", type=int, default=0,
                     help="independent index sets cycled over steps (0: enough that one cycle "
                          "selects more than 512 MiB of records, at least 4)")
@@ -265,7 +271,11 @@ def main():
     torch.cuda.set_device(dev)
 
     t_gen = time.perf_counter()
-    w = make_workload(args.config)
+    if args.batch > 0:
+        w = make_workload(dataclasses.replace(CONFIGS[args.config], batch=args.batch),
+                          seed=1000 + args.config)
+    else:
+        w = make_workload(args.config)
     spec = w["spec"]
     set_kv = 528.0 * (w["indices"] >= 0).sum() + (
         0.0 if w["extra_indices"] is None else 288.0 * (w["extra_indices"] >= 0).sum())
@@ -301,7 +311,8 @@ def main():
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record(stream)
-    md = mla.get_metadata(b, s, h, spec.topk, spec.extra_topk)
+    md = mla.get_metadata(b, s, h, spec.topk, spec.extra_topk,
+                          **({"num_parts": args.parts} if args.parts > 0 else {}))
     e1.record(stream)
     torch.cuda.synchronize()
     metadata_ms = e0.elapsed_time(e1)

@@ -23,6 +23,8 @@
 // Gathers, index loads, the raw-record and bf16 tile layouts and the dequantization are those of
 // the 128-head kernel.
 
+#include <type_traits>
+
 #include "mla_device.h"
 #include "mla_internal.h"
 
@@ -190,13 +192,6 @@ void sparse_decode_h64_kernel(DecodeParams p) {
   const int group_base = blockIdx.y * kGroupHeads;
   const int head_base = group_base + 16 * wave;                 // this wave's first QK^T head
   const uint64_t scale_lanes = 0xFFull << (8 * wave);           // scale chunks of tokens 8w..8w+7
-
-  // iteration -1 runs PV on tile slot 2, which no sub-tile has been written to, with zero
-  // probabilities: zeros keep those products finite (slots 0 and 1 are written before they are
-  // read)
-  for (int o = 2 * kTileBytes + threadIdx.x * 16; o < 3 * kTileBytes; o += 64 * kWaves * 16)
-    *reinterpret_cast<u32x4*>(tiles + o) = u32x4{};
-  __syncthreads();
 
   int row, t0, end_row, end_tile, slot_first;
   if (p.prefill_parts > 0) {
@@ -422,7 +417,10 @@ void sparse_decode_h64_kernel(DecodeParams p) {
       bf16x8 kb[kRing];
 
       // ---- one iteration (s in [-1, nsub)); r0, r1, r2 are the slots of sub-tiles s, s+1, s+2
-      auto iteration = [&](int s, int r0, int r1, int r2) {
+      auto iteration = [&](auto first, int s, int r0, int r1, int r2) {
+        // iteration -1 (first): there is no sub-tile -1, so it skips PV and the reads of its
+        // operands; tile slot 2 and the P^T buffer are then never read before they are written
+        constexpr bool kFirst = decltype(first)::value;
         const uint32_t ka[2] = {slot_base(k_addr[0], r1), slot_base(k_addr[1], r1)};
         const uint32_t va[2] = {slot_base(v_addr[0], r0), slot_base(v_addr[1], r0)};
         // V^T operand n (0..7): token half n / 4, this wave's dim block n % 4
@@ -470,11 +468,11 @@ void sparse_decode_h64_kernel(DecodeParams p) {
             kb[st % kRing] = lds_b128(ka[st & 1] + 64 * (st >> 1));
           }
           // phase B's first operands
-          if (i == 27) vv[0] = read_v(0);
-          if (i == 28) p0[0] = lds_b128(p_rd);
-          if (i == 29) vv[1] = read_v(1);
-          if (i == 30) p0[1] = lds_b128(p_rd + 2048);
-          if (i == 31) vv[2] = read_v(2);
+          if (!kFirst && i == 27) vv[0] = read_v(0);
+          if (!kFirst && i == 28) p0[0] = lds_b128(p_rd);
+          if (!kFirst && i == 29) vv[1] = read_v(1);
+          if (!kFirst && i == 30) p0[1] = lds_b128(p_rd + 2048);
+          if (!kFirst && i == 31) vv[2] = read_v(2);
           if ((i & 1) == 0) asm volatile("" ::"v"(kb[(i + 1) % kRing]));
           if (i < 2) mfma_qk16_first(sacc[i], kb[i % kRing], qreg[0]);
           else mfma_qk16(sacc[i & 1], kb[i % kRing], qreg[i >> 1]);
@@ -533,16 +531,18 @@ void sparse_decode_h64_kernel(DecodeParams p) {
         for (int i = 0; i < 16; ++i) {
           // V^T operand n is read five steps before its first use (step 2n), P^T of the second
           // token half at steps 3 and 4
-          if (i == 1) vv[3] = read_v(3);
-          if (i == 3) vv[0] = read_v(4);
-          if (i == 5) vv[1] = read_v(5);
-          if (i == 7) vv[2] = read_v(6);
-          if (i == 9) vv[3] = read_v(7);
-          if (i == 3) p1[0] = lds_b128(p_rd + 1024);
-          if (i == 4) p1[1] = lds_b128(p_rd + 3072);
-          if (i == 0) asm volatile("" ::"v"(p0[0]), "v"(p0[1]), "v"(vv[0]));
-          if (i == 8) asm volatile("" ::"v"(p1[0]), "v"(p1[1]), "v"(vv[0]));
-          mfma_pv32(oacc[i & 7], vv[(i >> 1) & 3], (i < 8 ? p0 : p1)[i & 1]);
+          if (!kFirst) {
+            if (i == 1) vv[3] = read_v(3);
+            if (i == 3) vv[0] = read_v(4);
+            if (i == 5) vv[1] = read_v(5);
+            if (i == 7) vv[2] = read_v(6);
+            if (i == 9) vv[3] = read_v(7);
+            if (i == 3) p1[0] = lds_b128(p_rd + 1024);
+            if (i == 4) p1[1] = lds_b128(p_rd + 3072);
+            if (i == 0) asm volatile("" ::"v"(p0[0]), "v"(p0[1]), "v"(vv[0]));
+            if (i == 8) asm volatile("" ::"v"(p1[0]), "v"(p1[1]), "v"(vv[0]));
+            mfma_pv32(oacc[i & 7], vv[(i >> 1) & 3], (i < 8 ? p0 : p1)[i & 1]);
+          }
           if (i == 0) {
             // scores: 20 wait states after the last QK^T MFMA before VALU reads them; ignored
             // tokens of a partially valid sub-tile take the ignored score
@@ -646,9 +646,6 @@ void sparse_decode_h64_kernel(DecodeParams p) {
               __builtin_bit_cast(u32x4, dequant_fp8_8(r[2], r[3], sb));
         }
       }
-      // zero P^T operands for the PV of iteration -1
-      for (int o = 16 * (64 * wave + lane64()); o < kPBytes; o += 16 * 64 * kWaves)
-        *reinterpret_cast<u32x4*>(smem + kOffP + o) = u32x4{};
       wait_barrier(0);
       mk0 = 0u;
       mk1 = mk_first[0];
@@ -669,16 +666,19 @@ void sparse_decode_h64_kernel(DecodeParams p) {
         r1 = r2;
         r2 = r_old;
       };
-      // three iterations with constant slots repeat, so every slot offset is a constant
+      // after iteration -1, three iterations with constant slots repeat, so every slot offset is
+      // a constant
+      iteration(std::true_type{}, -1, 2, 0, 1);
+      rotate();
 #pragma clang loop unroll(disable)
-      for (int s = -1; s < nsub; s += 3) {
-        iteration(s, 2, 0, 1);
+      for (int s = 0; s < nsub; s += 3) {
+        iteration(std::false_type{}, s, 0, 1, 2);
         rotate();
         if (s + 1 >= nsub) break;
-        iteration(s + 1, 0, 1, 2);
+        iteration(std::false_type{}, s + 1, 1, 2, 0);
         rotate();
         if (s + 2 >= nsub) break;
-        iteration(s + 2, 1, 2, 0);
+        iteration(std::false_type{}, s + 2, 2, 0, 1);
         rotate();
       }
       // O is read by VALU instructions below (20 wait states after the last PV MFMA); the last

@@ -32,6 +32,8 @@
 // waits on them are the explicit vmcnt waits at the iteration barrier, whose counts follow the
 // issue order (loads complete in order).
 
+#include <type_traits>
+
 #include "mla_device.h"
 #include "mla_internal.h"
 
@@ -545,16 +547,6 @@ void sparse_decode_wide_kernel(DecodeParams p) {
   // lanes of the scale-chunk copies: tokens 8w .. 8w+7 (first lane half; fp4: both halves)
   const uint64_t scale_lanes_fp8 = 0xFFull << (8 * wave);
   const uint64_t scale_lanes_fp4 = scale_lanes_fp8 | (scale_lanes_fp8 << 32);
-
-  if constexpr (!EXTRA) {
-    // The fp8 pipeline's first full iteration (-1) runs PV on tile slot 2, which no sub-tile has
-    // been written to yet, with zero probabilities: zeros keep those products finite (slots 0 and
-    // 1 are written before they are read). Later segments find finite data there (earlier
-    // sub-tiles, or the staged bf16 output).
-    for (int o = 2 * kTileBytes + threadIdx.x * 16; o < 3 * kTileBytes; o += 64 * kWaves * 16)
-      lds_write16(tiles + o, u32x4{});
-    __syncthreads();
-  }
 
   int row, t0, end_row, end_tile, slot_first;
   if (p.prefill_parts > 0) {
@@ -1130,7 +1122,10 @@ void sparse_decode_wide_kernel(DecodeParams p) {
       // barrier, so each piece stays next to its MFMA. Sub-tiles outside 0..nsub-1 take part with
       // an all-invalid mask: they gather from a valid dummy address, dequantize to zeros, get zero
       // probabilities and add nothing.
-      auto fp8_iteration = [&](int s, int r0, int r1, int r2) {
+      auto fp8_iteration = [&](auto first, int s, int r0, int r1, int r2) {
+        // iteration -1 (first): there is no sub-tile -1, so it skips PV and the reads of its
+        // operands; tile slot 2 and the P^T buffer are then never read before they are written
+        constexpr bool kFirst = decltype(first)::value;
         // operand addresses: K of sub-tile s+1 (phase A), V of sub-tile s (phase B); kb[0..2]
         // already hold the first three K operands
         // K of step kk at ka[kk % 2] + 64 (kk / 2), V of PV step n at va[h] + 16 kTileStride (n / 16)
@@ -1196,9 +1191,9 @@ void sparse_decode_wide_kernel(DecodeParams p) {
             // phase B's first operands: V^T 0 (step 27), P^T of the first token half of head
             // groups 0..3 (steps 27..30), V^T 1 (step 31)
             static_assert(kAhead == 5, "the reads below cover steps 32 - kAhead .. 31");
-            if (i == 27) vv[0] = read_v(0);
-            if (i < 31) p0[i - 27] = lds_k(p_rd + 2048 * (i - 27));
-            if (i == 31) vv[1] = read_v(1);
+            if (!kFirst && i == 27) vv[0] = read_v(0);
+            if (!kFirst && i < 31) p0[i - 27] = lds_k(p_rd + 2048 * (i - 27));
+            if (!kFirst && i == 31) vv[1] = read_v(1);
           }
           // operands are awaited in pairs: before an even step, the next step's operand too, so
           // that every other step needs no wait of its own
@@ -1284,12 +1279,14 @@ void sparse_decode_wide_kernel(DecodeParams p) {
         SoftmaxTemps st;
 #pragma unroll
         for (int i = 0; i < 32; ++i) {
-          if ((i + kAhead) % 4 == 0 && i + kAhead < 32) vv[((i + kAhead) / 4) % 3] = read_v((i + kAhead) / 4);
-          if (i >= 16 - kAhead && i < 20 - kAhead) p1[i - (16 - kAhead)] = lds_k(p_rd + 2048 * (i - (16 - kAhead)) + 1024);
+          if (!kFirst && (i + kAhead) % 4 == 0 && i + kAhead < 32) vv[((i + kAhead) / 4) % 3] = read_v((i + kAhead) / 4);
+          if (!kFirst && i >= 16 - kAhead && i < 20 - kAhead) p1[i - (16 - kAhead)] = lds_k(p_rd + 2048 * (i - (16 - kAhead)) + 1024);
           // each new operand set is awaited in one wait
-          if (i == 0) asm volatile("" ::"v"(p0[0]), "v"(p0[1]), "v"(p0[2]), "v"(p0[3]), "v"(vv[0]));
-          if (i == 16) asm volatile("" ::"v"(p1[0]), "v"(p1[1]), "v"(p1[2]), "v"(p1[3]), "v"(vv[1]));
-          mfma_pv(oacc[i & 15], vv[(i / 4) % 3], i < 16 ? p0[i & 3] : p1[i & 3]);
+          if (!kFirst) {
+            if (i == 0) asm volatile("" ::"v"(p0[0]), "v"(p0[1]), "v"(p0[2]), "v"(p0[3]), "v"(vv[0]));
+            if (i == 16) asm volatile("" ::"v"(p1[0]), "v"(p1[1]), "v"(p1[2]), "v"(p1[3]), "v"(vv[1]));
+            mfma_pv(oacc[i & 15], vv[(i / 4) % 3], i < 16 ? p0[i & 3] : p1[i & 3]);
+          }
           // the scores are read by VALU instructions next: 20 wait states after the last QK^T
           // MFMA (the PV MFMA above runs meanwhile)
           if (i == 0) asm volatile("s_nop 15\n\ts_nop 3" : "+v"(s_acc));
@@ -1356,10 +1353,6 @@ void sparse_decode_wide_kernel(DecodeParams p) {
             lds_write16(trow + 16 * ((2 * (c0 + cc) + 1) ^ sw), __builtin_bit_cast(u32x4, dequant_fp8_8(r[2], r[3], sb)));
           }
         }
-        // zero P^T operands for the PV of iteration -1, which runs on a tile slot no sub-tile of
-        // this pass has been written to
-        for (int o = 16 * (64 * wave + lane_id()); o < kPBytes; o += 16 * 64 * kWaves)
-          lds_write16(smem + L::kOffP + o, u32x4{});
         // tile 0 is complete and raw slot 0 free for the gather of sub-tile 3
         wait_and_barrier(0);
         mk0 = 0u;
@@ -1386,19 +1379,21 @@ void sparse_decode_wide_kernel(DecodeParams p) {
         r2 = r_old;
       };
       if constexpr (!EXTRA) {
-        // Iteration s works on slots s % 3, (s+1) % 3, (s+2) % 3; starting from s = -1, three
+        // Iteration s works on slots s % 3, (s+1) % 3, (s+2) % 3; after iteration -1, three
         // iterations with constant slots repeat, so every slot offset is a compile-time constant.
         // Each iteration's wait and barrier are issued by the previous iteration (every iteration
         // issues one index load and kGatherFp8 gather copies) or before the loop.
+        fp8_iteration(std::true_type{}, s_first, 2, 0, 1);
+        rotate();
 #pragma clang loop unroll(disable)
-        for (int s = s_first; s < nsub; s += 3) {
-          fp8_iteration(s, 2, 0, 1);
+        for (int s = s_first + 1; s < nsub; s += 3) {
+          fp8_iteration(std::false_type{}, s, 0, 1, 2);
           rotate();
           if (s + 1 >= nsub) break;
-          fp8_iteration(s + 1, 0, 1, 2);
+          fp8_iteration(std::false_type{}, s + 1, 1, 2, 0);
           rotate();
           if (s + 2 >= nsub) break;
-          fp8_iteration(s + 2, 1, 2, 0);
+          fp8_iteration(std::false_type{}, s + 2, 2, 0, 1);
           rotate();
         }
       }

@@ -23,12 +23,12 @@ int tiles_per_row(int topk, int extra_topk, int* tiles_k) {
 // 32 heads, one workgroup per CU); up to 64 heads run in one 64-head group of four waves of 16
 // heads, with heads past h_q masked, in one of two kernels:
 //  - mla_decode_h64.hip (fp8 records only): one software-pipelined sub-tile stream, one wave per
-//    SIMD; about 1.1 us per 32-token sub-tile, but some 3 us more than the other to start a part;
+//    SIMD; about 1.1 us per 32-token sub-tile, but a longer start than the other;
 //  - mla_decode.hip: two halves of four waves with a one-deep pipeline; about 1.6 us per sub-tile.
 // The first is taken when the parts average at least kStreamMinSubtiles sub-tiles (measured on
-// MI355X: ahead from 16 sub-tiles per part, behind at 8 with every CU busy).
+// MI355X over 32 rows of 64 heads: 3 us ahead at 8 sub-tiles per part, level at 4, behind at 2).
 bool wide_for(int h_q) { return h_q > 64; }
-constexpr int kStreamMinSubtiles = 12;
+constexpr int kStreamMinSubtiles = 6;
 bool h64_stream_for(int rows, int tiles, int parts, int extra_topk) {
   return extra_topk == 0 && 2 * (int64_t)rows * tiles >= (int64_t)kStreamMinSubtiles * parts;
 }

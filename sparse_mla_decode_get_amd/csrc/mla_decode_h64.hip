@@ -715,9 +715,10 @@ void sparse_decode_h64_kernel(DecodeParams p) {
         const float l = lsums[32 * hb + h];
         inv_b[hb] = l > 0.0f ? 1.0f / l : 0.0f;
       }
-      if (final_out) {
-        // head rows staged in bf16 (row hd at hd * kStageRow, 8-byte unit u at + 8u), then each
-        // wave stores the 1 KB rows of its own 16 heads
+      // head rows (the final output, or this split's normalised bf16 partial) staged in bf16 (row
+      // hd at hd * kStageRow, 8-byte unit u at + 8u), then each wave stores the 1 KB rows of its
+      // own 16 heads
+      {
         const uint32_t wbase = lds_a(smem + h * kStageRow + 8 * g) + 256 * wave;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
@@ -732,30 +733,14 @@ void sparse_decode_h64_kernel(DecodeParams p) {
         }
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
         const uint32_t rbase = lds_a(smem + 16 * wave * kStageRow) + 16 * lane;
-        char* const orow = reinterpret_cast<char*>(p.out) + ((int64_t)row * p.h_q + head_base) * (2 * kHeadDim);
+        char* const orow =
+            final_out ? reinterpret_cast<char*>(p.out) + ((int64_t)row * p.h_q + head_base) * (2 * kHeadDim)
+                      : static_cast<char*>(p.part_o) + ((int64_t)slot * p.h_q + head_base) * (2 * kHeadDim);
         for (int r = 0; r < 16 && head_base + r < p.h_q; ++r) {
           const bf16x4 lo = *reinterpret_cast<const lds_bf16x4_rw*>(rbase + r * kStageRow);
           const bf16x4 hi = *reinterpret_cast<const lds_bf16x4_rw*>(rbase + r * kStageRow + 8);
           *reinterpret_cast<bf16x8*>(orow + r * (2 * kHeadDim) + 16 * lane) =
               __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        }
-      } else {
-        // normalised bf16 partial of this split
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int hb = j & 1, b = j >> 1;
-          const int head_j = group_base + 32 * hb + h;
-          if (head_j < p.h_q) {
-#pragma unroll
-            for (int jb = 0; jb < 4; ++jb) {
-              const int dim = 32 * (4 * wave + b) + 8 * jb + 4 * g;
-              bf16x4 o;
-#pragma unroll
-              for (int i = 0; i < 4; ++i) o[i] = (__bf16)(oacc[j][4 * jb + i] * inv_b[hb]);
-              *reinterpret_cast<bf16x4*>(static_cast<uint16_t*>(p.part_o) +
-                                         ((int64_t)slot * p.h_q + head_j) * kHeadDim + dim) = o;
-            }
-          }
         }
       }
       const int head = head_base + (lane & 15);

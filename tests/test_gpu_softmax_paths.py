@@ -185,7 +185,7 @@ STREAM_CASES = [
 
 @pytest.mark.parametrize("name,h_q,mode", STREAM_CASES, ids=[c[0] for c in STREAM_CASES])
 def test_score_growth_single_stream_64_head_kernel(name, h_q, mode):
-    """The single-stream 64-head kernel (fp8 only, parts of at least 12 sub-tiles) takes
+    """The single-stream 64-head kernel (fp8 only, parts of at least 6 sub-tiles) takes
     probabilities against each head's first live sub-tile like the 128-head kernel: "extreme" rows
     grow by more than 64 log2 units past it, which forces the second pass."""
     spec = Spec(name, 4, 1, h_q, 1024, 8192)

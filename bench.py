@@ -43,9 +43,10 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 METRIC = "sparse MLA decode TFLOP/s + KV GB/s, fp8 528B/tok, B=128 H=128 topk=2048"
 CSRC = os.path.join(ROOT, "sparse_mla_decode_get_amd", "csrc")
-# decode kernel source (and the headers it includes) for head counts above 64 and up to 64
+# decode kernel sources (and the headers they include) for head counts above 64 and up to 64 (the
+# single-stream and the two-half kernel, either of which the schedule may select)
 DECODE_SRCS = {True: ["mla_decode_wide.hip", "mla_device.h", "mla_internal.h"],
-               False: ["mla_decode.hip", "mla_device.h", "mla_internal.h"]}
+               False: ["mla_decode_h64.hip", "mla_decode.hip", "mla_device.h", "mla_internal.h"]}
 
 
 def kernel_source_hash(wide: bool) -> str:

@@ -1579,10 +1579,32 @@ void sparse_decode_wide_kernel(DecodeParams p) {
           *reinterpret_cast<bf16x8*>(orow + r * (2 * kHeadDim) + 16 * lane) =
               __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         }
+      } else if constexpr (!FUSED) {
+        // the normalised bf16 partial of this split, staged like the final rows
+        const uint32_t wbase = lds_addr(smem + h * kStageRow + 8 * g);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const uint32_t jbase = wbase + blk_hg(j) * kStageBytes + 64 * blk_d(j);
+          const float inv = inv_of(j);
+#pragma unroll
+          for (int jb = 0; jb < 4; ++jb) {
+            bf16x4 o;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[i] = (__bf16)(oacc[j][4 * jb + i] * inv);
+            *reinterpret_cast<lds_bf16x4_w*>(jbase + 16 * jb) = o;
+          }
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        const uint32_t rbase = lds_addr(smem + wave * kStageBytes + 16 * lane);
+        char* const prow = static_cast<char*>(p.part_o) + ((int64_t)slot * p.h_q + head_base) * (2 * kHeadDim);
+        for (int r = 0; r < 32 && head_base + r < p.h_q; ++r) {
+          const bf16x4 lo = *reinterpret_cast<const lds_bf16x4_w*>(rbase + r * kStageRow);
+          const bf16x4 hi = *reinterpret_cast<const lds_bf16x4_w*>(rbase + r * kStageRow + 8);
+          *reinterpret_cast<bf16x8*>(prow + r * (2 * kHeadDim) + 16 * lane) =
+              __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
       } else {
-        // the normalised partial of this split: bf16 for the merge of the plain decode (its
-        // rounding, 2^-9 relative, is far inside the output tolerance, and it halves the partial
-        // traffic), fp32 for the fused decode's merge, which encodes fp8 records from it
+        // the fused decode's fp32 partial, which its merge encodes into fp8 records
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
           const int head_j = blockIdx.y * kGroupHeads + 32 * blk_hg(j) + h;
@@ -1592,17 +1614,10 @@ void sparse_decode_wide_kernel(DecodeParams p) {
 #pragma unroll
             for (int jb = 0; jb < 4; ++jb) {
               const int dim = 32 * blk_d(j) + 8 * jb + 4 * g;
-              if constexpr (FUSED) {
-                f32x4 o;
+              f32x4 o;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) o[i] = oacc[j][4 * jb + i] * inv;
-                *reinterpret_cast<f32x4*>(static_cast<float*>(p.part_o) + base + dim) = o;
-              } else {
-                bf16x4 o;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) o[i] = (__bf16)(oacc[j][4 * jb + i] * inv);
-                *reinterpret_cast<bf16x4*>(static_cast<uint16_t*>(p.part_o) + base + dim) = o;
-              }
+              for (int i = 0; i < 4; ++i) o[i] = oacc[j][4 * jb + i] * inv;
+              *reinterpret_cast<f32x4*>(static_cast<float*>(p.part_o) + base + dim) = o;
             }
           }
           __builtin_amdgcn_sched_barrier(0);

@@ -1,10 +1,10 @@
-// Sparse MLA decode kernel for gfx950, 64-head groups of fp8 records (h_q <= 64, no extra cache).
+// Sparse MLA decode kernel for gfx950, 64-head groups (h_q <= 64).
 //
 // Same computation as the other decode kernels (page "flops/flashmla-decode-fp8-fp4-kv", sections
 // "Arithmetic intensity" and "Workarounds"; page "deepseek-ai/FlashMLA", section "Key technical
 // details"): per query row and head, one softmax over the row's selected tokens, key and value both
-// the 512-dim latent decoded from the token's 528-byte record, negative indices ignored, natural-log
-// lse returned beside the output.
+// the 512-dim latent decoded from the token's 528-byte fp8 record (or 288-byte fp4 record of the
+// extra cache), negative indices ignored, natural-log lse returned beside the output.
 //
 // The software pipeline is the one of the 128-head kernel (mla_decode_wide.hip), cut to 64 heads:
 // one workgroup of 4 waves per CU, one wave per SIMD, one stream of 32-token sub-tiles. Wave w owns
@@ -21,7 +21,10 @@
 //   phase B  the 16 PV MFMAs of sub-tile s (32x32x16), with the softmax of s+1, the other half of
 //            the dequantization and the K operands of the next QK^T between them.
 // Gathers, index loads, the raw-record and bf16 tile layouts and the dequantization are those of
-// the 128-head kernel.
+// the 128-head kernel. With an extra cache (EXTRA) a segment's units past the row's fp8 units are
+// fp4 units; the choice is made per sub-tile with wave-uniform branches, and an fp4 sub-tile issues
+// the same five record copies as an fp8 one (two of them read the zero record into chunks the fp4
+// layout leaves unused), so the fixed s_waitcnt counts hold for any mix.
 
 #include <type_traits>
 
@@ -179,6 +182,25 @@ __device__ __forceinline__ float sum_xor16(float x) {
   return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
 }
 
+// Where sub-tile j of a segment that starts at unit t0 takes its entries: the extra (fp4) cache
+// when its unit lies past the row's tiles_k fp8 units; pos0 is its first entry in that cache's
+// index row of `count` entries.
+struct SubTile {
+  bool x;
+  int pos0;
+  int count;
+};
+template <bool EXTRA>
+__device__ __forceinline__ SubTile locate(const DecodeParams& p, int t0, int j) {
+  // unit t0 + j / 2 is an fp4 one when t0 + j / 2 >= tiles_k, i.e. when 2 t0 + j >= 2 tiles_k
+  SubTile st;
+  st.x = EXTRA && 2 * t0 + j >= 2 * p.tiles_k;
+  st.pos0 = kUnitTokens * (st.x ? t0 - p.tiles_k : t0) + kSubTokens * j;
+  st.count = st.x ? p.extra_topk : p.topk;
+  return st;
+}
+
+template <bool EXTRA>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void sparse_decode_h64_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
@@ -192,6 +214,7 @@ void sparse_decode_h64_kernel(DecodeParams p) {
   const int group_base = blockIdx.y * kGroupHeads;
   const int head_base = group_base + 16 * wave;                 // this wave's first QK^T head
   const uint64_t scale_lanes = 0xFFull << (8 * wave);           // scale chunks of tokens 8w..8w+7
+  const uint64_t scale_lanes_x = scale_lanes | (scale_lanes << 32);  // fp4: both 16 B scale halves
 
   int row, t0, end_row, end_tile, slot_first;
   if (p.prefill_parts > 0) {
@@ -221,9 +244,10 @@ void sparse_decode_h64_kernel(DecodeParams p) {
     // (clamped addresses; a selection of size 0 reads the schedule instead)
     auto load_indices = [&](int j, int slot) {
       const int e = 8 * wave + (lane64() & 7);
+      const SubTile st = locate<EXTRA>(p, t0, j);
       const int32_t* src_ptr = p.sched;
-      if (j < nsub && p.topk > 0)
-        src_ptr = p.idx + (int64_t)row * p.topk + min(kUnitTokens * t0 + kSubTokens * j + e, p.topk - 1);
+      if (j < nsub && st.count > 0)
+        src_ptr = (st.x ? p.xidx : p.idx) + (int64_t)row * st.count + min(st.pos0 + e, st.count - 1);
       g2l4_masked(src_ptr, __builtin_amdgcn_readfirstlane(lds_a(idx_ring + slot * kIdxBytes) + 32 * wave),
                   0xFFull);
     };
@@ -237,9 +261,17 @@ void sparse_decode_h64_kernel(DecodeParams p) {
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int e = e0 + 64 * kWaves * u + tid;
-        const int pos = kUnitTokens * t0 + e;
-        in[u] = e / kSubTokens < nsub_all && pos < p.topk;
-        src[u] = p.topk > 0 ? p.idx + (int64_t)row * p.topk + min(pos, p.topk - 1) : p.sched;
+        if constexpr (EXTRA) {
+          const SubTile st = locate<EXTRA>(p, t0, min(e / kSubTokens, nsub_all - 1));
+          const int pos = st.pos0 + e % kSubTokens;
+          in[u] = e / kSubTokens < nsub_all && pos < st.count;
+          src[u] = st.count > 0 ? (st.x ? p.xidx : p.idx) + (int64_t)row * st.count + min(pos, st.count - 1)
+                                : p.sched;
+        } else {
+          const int pos = kUnitTokens * t0 + e;
+          in[u] = e / kSubTokens < nsub_all && pos < p.topk;
+          src[u] = p.topk > 0 ? p.idx + (int64_t)row * p.topk + min(pos, p.topk - 1) : p.sched;
+        }
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u) v[u] = *src[u];
@@ -250,17 +282,26 @@ void sparse_decode_h64_kernel(DecodeParams p) {
     auto gather_first = [&](int j, int live) -> uint32_t {
       const int lane = lane64();
       const int t = lane & 31, hh = lane >> 5;
+      const SubTile st = locate<EXTRA>(p, t0, j);
       const int gv = *reinterpret_cast<const int*>(idx_ring + j * kIdxBytes + 4 * t);
-      const bool valid = j < live && p.topk > 0 && kUnitTokens * t0 + kSubTokens * j + t < p.topk && gv >= 0;
+      const bool valid = j < live && st.pos0 + t < st.count && gv >= 0;
       const uint32_t mask = (uint32_t)__ballot(valid);
-      const uint8_t* grec = valid ? p.kc + (int64_t)gv * kFp8Rec : g_zero64.bytes;
-      const uint8_t* gdat = grec + 32 * wave + 16 * hh;
       const uint32_t graw = lds_a(smem) + kOffRaw + j * kRawBytes;
-      g2l16_off<0>(gdat, graw + 1024 * wave);
-      g2l16_off<128>(gdat, graw + 1024 * (wave + 4));
-      g2l16_off<256>(gdat, graw + 1024 * (wave + 8));
-      g2l16_off<384>(gdat, graw + 1024 * (wave + 12));
-      g2l16_masked(grec + 512, graw + 32 * 512, scale_lanes);
+      if (EXTRA && st.x) {
+        const uint8_t* grec = valid ? p.xc + (int64_t)gv * kFp4Rec : g_zero64.bytes;
+        const uint8_t* gdat = grec + 32 * wave + 16 * hh;
+        g2l16_off<0>(gdat, graw + 1024 * wave);
+        g2l16_off<128>(gdat, graw + 1024 * (wave + 4));
+        g2l16_masked(grec + 256 + 16 * hh, graw + 16 * 512, scale_lanes_x);
+      } else {
+        const uint8_t* grec = valid ? p.kc + (int64_t)gv * kFp8Rec : g_zero64.bytes;
+        const uint8_t* gdat = grec + 32 * wave + 16 * hh;
+        g2l16_off<0>(gdat, graw + 1024 * wave);
+        g2l16_off<128>(gdat, graw + 1024 * (wave + 4));
+        g2l16_off<256>(gdat, graw + 1024 * (wave + 8));
+        g2l16_off<384>(gdat, graw + 1024 * (wave + 12));
+        g2l16_masked(grec + 512, graw + 32 * 512, scale_lanes);
+      }
       return mask;
     };
     uint32_t mk_first[3] = {0u, 0u, 0u};
@@ -334,12 +375,13 @@ void sparse_decode_h64_kernel(DecodeParams p) {
     //              + 64 b + 16 kTileStride ks: token row 16 ks + 8((l/16)/2) + 4h + (l%16)/4,
     //              logical chunk 16 w + 4 b + 2((l/16)%2) + (l%4)/2, 8-byte half l%2
     //  dq_w[m]     the lane's bf16 chunks of its dequantization (chunk 2 c0 + j at dq_w[j % 4]
-    //              + 64 (j / 4)); raw_r / raw_s its fp8 chunk and scale bytes (token t)
+    //              + 64 (j / 4)); raw_r / raw_s its fp8 chunk and scale bytes (token t);
+    //              raw_r4 / raw_s4 its fp4 chunks 4w + 2hh, +1 and e4m3 scale bytes 8w + 4hh .. +3
     //  idx_r       index entry of token t; idx_v its byte offset in a 32-entry block; idx_l the
     //              byte offset of the entry this lane loads into the shared ring
     //  g_base / g_zb  record byte 32 w + 16 hh of record 0 of the cache / of the zero record
     //  p_rd        P^T exchange buffer, this lane's 16 bytes of head block 0, token half 0
-    uint32_t k_addr[2], v_addr[2], dq_w[4], raw_r, raw_s, idx_r, idx_v, idx_l, p_rd;
+    uint32_t k_addr[2], v_addr[2], dq_w[4], raw_r, raw_s, raw_r4 = 0, raw_s4 = 0, idx_r, idx_v, idx_l, p_rd;
     uint64_t g_base, g_zb;
     {
       const int lane = lane64();
@@ -372,8 +414,15 @@ void sparse_decode_h64_kernel(DecodeParams p) {
                    "+v"(dq_w[0]), "+v"(dq_w[1]), "+v"(dq_w[2]), "+v"(dq_w[3]), "+v"(raw_r),
                    "+v"(raw_s), "+v"(idx_r), "+v"(idx_v), "+v"(idx_l), "+v"(p_rd), "+v"(g_base),
                    "+v"(g_zb));
+      if constexpr (EXTRA) {
+        raw_r4 = lds_a(raws + ((4 * wave + 2 * hh) * kSubTokens + t) * 16);
+        raw_s4 = lds_a(raws + ((16 + (wave >> 1)) * kSubTokens + t) * 16 + 8 * (wave & 1) + 4 * hh);
+        asm volatile("" : "+v"(raw_r4), "+v"(raw_s4));
+      }
     }
     const uint64_t idx_row = (uint64_t)(uintptr_t)(p.idx + (int64_t)row * p.topk);
+    const uint64_t xidx_row = EXTRA ? (uint64_t)(uintptr_t)(p.xidx + (int64_t)row * p.extra_topk) : 0;
+    const uint64_t x_delta = EXTRA ? (uint64_t)(uintptr_t)p.xc - (uint64_t)(uintptr_t)p.kc : 0;
     // operand base of slot sl; slot 2 starts past 64 KB, so its base is formed in a register
     auto slot_base = [&](uint32_t base, int sl) -> uint32_t {
       uint32_t a = base + sl * kTileBytes;
@@ -421,6 +470,8 @@ void sparse_decode_h64_kernel(DecodeParams p) {
         // iteration -1 (first): there is no sub-tile -1, so it skips PV and the reads of its
         // operands; tile slot 2 and the P^T buffer are then never read before they are written
         constexpr bool kFirst = decltype(first)::value;
+        // sub-tile s+2, dequantized in this iteration, is an fp4 one
+        const bool dx = EXTRA && __builtin_amdgcn_readfirstlane(locate<EXTRA>(p, t0, s + 2).x ? 1 : 0) != 0;
         const uint32_t ka[2] = {slot_base(k_addr[0], r1), slot_base(k_addr[1], r1)};
         const uint32_t va[2] = {slot_base(v_addr[0], r0), slot_base(v_addr[1], r0)};
         // V^T operand n (0..7): token half n / 4, this wave's dim block n % 4
@@ -437,10 +488,35 @@ void sparse_decode_h64_kernel(DecodeParams p) {
 #pragma unroll
         for (int m = 0; m < 4; ++m) dqa[m] = slot_base(dq_w[m], r2);
         uint32_t sc2 = 0;
-        u32x4 rr0, rr1;
+        u32x4 rr0, rr1, fr0, fr1;
         bf16x8 dlo, dhi;
+        u32x4 flo, fhi;
+        float fsc = 0.0f;
+        // step k of 16: quarter k % 4 of the lane's 16-value block k / 4 (fp8: two steps convert,
+        // one writes; fp4: four e2m1 values times the block's e4m3 scale per step, written at the end)
         auto dequant_step = [&](int k) {
           const int cc = k >> 2, part = k & 3;
+          if (EXTRA && dx) {
+            const u32x4& r = (cc >> 1) ? fr1 : fr0;
+            const uint32_t w = r[2 * (cc & 1) + (part >> 1)];
+            if (part == 0) fsc = e4m3_to_f32(sc2 >> (8 * cc));
+            uint32_t a, b;
+            if (part & 1) {
+              a = __builtin_bit_cast(uint32_t, fp4_byte<2>(w, fsc));
+              b = __builtin_bit_cast(uint32_t, fp4_byte<3>(w, fsc));
+            } else {
+              a = __builtin_bit_cast(uint32_t, fp4_byte<0>(w, fsc));
+              b = __builtin_bit_cast(uint32_t, fp4_byte<1>(w, fsc));
+            }
+            u32x4& d = (part >> 1) ? fhi : flo;
+            d[2 * (part & 1)] = a;
+            d[2 * (part & 1) + 1] = b;
+            if (part == 3) {
+              lds_w16(dqa[(2 * cc) & 3] + 64 * ((2 * cc) >> 2), flo);
+              lds_w16(dqa[(2 * cc + 1) & 3] + 64 * ((2 * cc + 1) >> 2), fhi);
+            }
+            return;
+          }
           const uint32_t sb = (sc2 >> (8 * (cc >> 1))) & 0xFFu;
           const u32x4& r = (cc & 1) ? rr1 : rr0;
           if (part == 0) dlo = dequant_fp8_8(r[0], r[1], sb);
@@ -450,12 +526,14 @@ void sparse_decode_h64_kernel(DecodeParams p) {
             lds_w16(dqa[(2 * cc + 1) & 3] + 64 * ((2 * cc + 1) >> 2), __builtin_bit_cast(u32x4, dhi));
           }
         };
-        // gather of s+4 (index slot r1 -> raw slot r1)
-        const int g_pos0 = kUnitTokens * t0 + kSubTokens * (s + 4);
-        const int g_lim = (s + 4 < nsub && p.topk > g_pos0) ? p.topk - g_pos0 : 0;
+        // gather of s+4 (index slot r1 -> raw slot r1); gdat2 is the source of copies 2 and 3, the
+        // zero record for an fp4 sub-tile (its 256 data bytes are copies 0 and 1)
+        const SubTile gs = locate<EXTRA>(p, t0, s + 4);
+        const bool gx = EXTRA && gs.x;
+        const int g_lim = (s + 4 < nsub && gs.count > gs.pos0) ? gs.count - gs.pos0 : 0;
         const uint32_t graw = lds_a(smem) + kOffRaw + r1 * kRawBytes;
         int gv = 0;
-        uint64_t gdat = 0;
+        uint64_t gdat = 0, gdat2 = 0;
 
         // phase A: QK^T of sub-tile s+1, step i = token block i % 2 of k-step i / 2
 #pragma unroll
@@ -477,38 +555,54 @@ void sparse_decode_h64_kernel(DecodeParams p) {
           if (i < 2) mfma_qk16_first(sacc[i], kb[i % kRing], qreg[0]);
           else mfma_qk16(sacc[i & 1], kb[i % kRing], qreg[i >> 1]);
           if (i == 1) {
-            sc2 = *reinterpret_cast<const __attribute__((address_space(3))) uint16_t*>(
-                (uintptr_t)(raw_s + r2 * kRawBytes));
-            rr0 = *(lds_u32x4_r*)(uintptr_t)(draw);
-            rr1 = *(lds_u32x4_r*)(uintptr_t)(draw + 512);
+            if (EXTRA && dx) {
+              const uint32_t draw4 = raw_r4 + r2 * kRawBytes;
+              sc2 = *reinterpret_cast<const __attribute__((address_space(3))) uint32_t*>(
+                  (uintptr_t)(raw_s4 + r2 * kRawBytes));
+              fr0 = *(lds_u32x4_r*)(uintptr_t)(draw4);
+              fr1 = *(lds_u32x4_r*)(uintptr_t)(draw4 + 512);
+            } else {
+              sc2 = *reinterpret_cast<const __attribute__((address_space(3))) uint16_t*>(
+                  (uintptr_t)(raw_s + r2 * kRawBytes));
+              rr0 = *(lds_u32x4_r*)(uintptr_t)(draw);
+              rr1 = *(lds_u32x4_r*)(uintptr_t)(draw + 512);
+            }
             gv = *reinterpret_cast<const __attribute__((address_space(3))) int*>(
                 (uintptr_t)(idx_r + r1 * kIdxBytes));
           } else if (i == 3) {
             const bool valid = idx_v < (uint32_t)(4 * g_lim) && gv >= 0;
             mk4 = (uint32_t)__ballot(valid);
-            const uint64_t a = g_base + (uint64_t)(int64_t)gv * kFp8Rec;
+            const uint64_t a =
+                g_base + (gx ? x_delta : 0ull) + (uint64_t)(int64_t)gv * (gx ? kFp4Rec : kFp8Rec);
             gdat = valid ? a : g_zb;
+            gdat2 = gx ? g_zb : gdat;
           }
           // gather copies at steps 4, 9, 14, 19 (chunk pairs 2(w + 4c) + hh) and 24 (scale chunks of
-          // tokens 8w .. 8w+7: the record's byte 512 is 512 - 32 w past gdat)
+          // tokens 8w .. 8w+7: the record's byte 512 is 512 - 32 w past gdat; fp4: both halves of
+          // the 32 scale bytes at byte 256, into chunks 16 and 17)
           if (i >= 4 && i < 24 && (i - 4) % 5 == 0) {
             const int c = (i - 4) / 5;
-            const uint32_t dst = __builtin_amdgcn_readfirstlane(graw + 1024 * (wave + 4 * c));
+            // an fp4 sub-tile's copy 2 lands on copy 3's chunks (unused by it), clear of chunks 16, 17
+            const int cd = (gx && c == 2) ? 3 : c;
+            const uint32_t dst = __builtin_amdgcn_readfirstlane(graw + 1024 * (wave + 4 * cd));
             const void* gp = (const void*)(uintptr_t)gdat;
+            const void* gp2 = (const void*)(uintptr_t)gdat2;
             if (c == 0) g2l16_off<0>(gp, dst);
             else if (c == 1) g2l16_off<128>(gp, dst);
-            else if (c == 2) g2l16_off<256>(gp, dst);
-            else g2l16_off<384>(gp, dst);
+            else if (c == 2) g2l16_off<256>(gp2, dst);
+            else g2l16_off<384>(gp2, dst);
           } else if (i == 24) {
-            g2l16_masked((const void*)(uintptr_t)(gdat + (uint64_t)(512 - 32 * wave)),
-                         __builtin_amdgcn_readfirstlane(graw + 32 * 512), scale_lanes);
+            const int sofs = (gx ? 256 : 512) - 32 * wave;
+            g2l16_masked((const void*)(uintptr_t)(gdat + (uint64_t)(int64_t)sofs),
+                         __builtin_amdgcn_readfirstlane(graw + (gx ? 16 : 32) * 512),
+                         gx ? scale_lanes_x : scale_lanes);
           }
           if (i == 26) {
             // index load of sub-tile s+6 into this wave's quarter of index slot r0, from a buffer
             // that ends at the index row's end (empty past the live segment)
-            const int pos = kUnitTokens * t0 + kSubTokens * (s + 6);
-            const int n_in = (s + 6 < nsub && p.topk > pos) ? p.topk - pos : 0;
-            const uint64_t base = idx_row + (uint64_t)(4 * (int64_t)pos);
+            const SubTile is = locate<EXTRA>(p, t0, s + 6);
+            const int n_in = (s + 6 < nsub && is.count > is.pos0) ? is.count - is.pos0 : 0;
+            const uint64_t base = (EXTRA && is.x ? xidx_row : idx_row) + (uint64_t)(4 * (int64_t)is.pos0);
             const u32x4 rsrc = {(uint32_t)base, (uint32_t)(base >> 32) & 0xFFFFu, (uint32_t)(4 * n_in),
                                 0x00020000u};
             buf2l4(rsrc, idx_l, lds_a(smem) + kOffIdx + r0 * kIdxBytes + 32 * wave, 0xFFull);
@@ -634,16 +728,34 @@ void sparse_decode_h64_kernel(DecodeParams p) {
         const int t = lane & 31, hh = lane >> 5;
         char* trow = tiles + t * kTileStride;
         const int sw = xor64(t);
-        const int c0 = 8 * wave + 4 * hh;
-        const uint32_t s2 = *reinterpret_cast<const uint16_t*>(raws + (32 * kSubTokens + t) * 16 + c0 / 2);
+        if (EXTRA && locate<EXTRA>(p, t0, 0).x) {
+          // fp4: raw chunks c0, c0 + 1 (32 e2m1 values each) with e4m3 scale bytes j0 .. j0 + 3
+          const int c0 = 4 * wave + 2 * hh, j0 = 8 * wave + 4 * hh;
+          const uint32_t s4 = *reinterpret_cast<const uint32_t*>(
+              raws + ((16 + (j0 >> 4)) * kSubTokens + t) * 16 + (j0 & 15));
 #pragma unroll
-        for (int cc = 0; cc < 4; ++cc) {
-          const u32x4 r = *reinterpret_cast<const u32x4*>(raws + ((c0 + cc) * kSubTokens + t) * 16);
-          const uint32_t sb = (s2 >> (8 * (cc >> 1))) & 0xFFu;
-          *reinterpret_cast<u32x4*>(trow + 16 * ((2 * (c0 + cc)) ^ sw)) =
-              __builtin_bit_cast(u32x4, dequant_fp8_8(r[0], r[1], sb));
-          *reinterpret_cast<u32x4*>(trow + 16 * ((2 * (c0 + cc) + 1) ^ sw)) =
-              __builtin_bit_cast(u32x4, dequant_fp8_8(r[2], r[3], sb));
+          for (int cc = 0; cc < 2; ++cc) {
+            const u32x4 r = *reinterpret_cast<const u32x4*>(raws + ((c0 + cc) * kSubTokens + t) * 16);
+            bf16x8 a[4];
+            dequant_fp4_16(r[0], r[1], e4m3_to_f32(s4 >> (16 * cc)), a[0], a[1]);
+            dequant_fp4_16(r[2], r[3], e4m3_to_f32(s4 >> (16 * cc + 8)), a[2], a[3]);
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+              *reinterpret_cast<u32x4*>(trow + 16 * (4 * (c0 + cc) + (m ^ sw))) =
+                  __builtin_bit_cast(u32x4, a[m]);
+          }
+        } else {
+          const int c0 = 8 * wave + 4 * hh;
+          const uint32_t s2 = *reinterpret_cast<const uint16_t*>(raws + (32 * kSubTokens + t) * 16 + c0 / 2);
+#pragma unroll
+          for (int cc = 0; cc < 4; ++cc) {
+            const u32x4 r = *reinterpret_cast<const u32x4*>(raws + ((c0 + cc) * kSubTokens + t) * 16);
+            const uint32_t sb = (s2 >> (8 * (cc >> 1))) & 0xFFu;
+            *reinterpret_cast<u32x4*>(trow + 16 * ((2 * (c0 + cc)) ^ sw)) =
+                __builtin_bit_cast(u32x4, dequant_fp8_8(r[0], r[1], sb));
+            *reinterpret_cast<u32x4*>(trow + 16 * ((2 * (c0 + cc) + 1) ^ sw)) =
+                __builtin_bit_cast(u32x4, dequant_fp8_8(r[2], r[3], sb));
+          }
         }
       }
       wait_barrier(0);
@@ -762,7 +874,10 @@ void sparse_decode_h64_kernel(DecodeParams p) {
 }  // namespace
 
 int launch_sparse_decode_h64(const DecodeParams& p, int parts, int groups, hipStream_t stream) {
-  hipLaunchKernelGGL(sparse_decode_h64_kernel, dim3(parts, groups), dim3(64 * kWaves), 0, stream, p);
+  if (p.extra_topk > 0)
+    hipLaunchKernelGGL(sparse_decode_h64_kernel<true>, dim3(parts, groups), dim3(64 * kWaves), 0, stream, p);
+  else
+    hipLaunchKernelGGL(sparse_decode_h64_kernel<false>, dim3(parts, groups), dim3(64 * kWaves), 0, stream, p);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

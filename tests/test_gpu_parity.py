@@ -356,10 +356,9 @@ def test_decode_replays_from_a_captured_graph(h_q):
 
 
 # ------------------------------------------------ the single-stream 64-head kernel (mla_decode_h64)
-# h_q <= 64 without an extra cache runs in that kernel when the parts average at least 6 sub-tiles
-# of 32 tokens (2 * rows * units / parts >= 6), as the default schedules of fp8-only shapes do; the
-# cases below are sized for it. Parts of fewer sub-tiles, and every decode with an extra cache, run
-# the two-half kernel (mla_decode.hip).
+# h_q <= 64 runs in that kernel when the parts average at least 6 sub-tiles of 32 tokens of either
+# cache (2 * rows * units / parts >= 6), as the default schedules of the larger shapes do; the cases
+# below are sized for it. Parts of fewer sub-tiles run the two-half kernel (mla_decode.hip).
 
 def _stream_parts(spec, per_part):
     """A part count that gives `per_part` sub-tiles per part (at least 6), units of both caches."""
@@ -418,8 +417,8 @@ def test_stream_64_head_trailing_ignored_subtiles(per_part):
     (Spec("long_parts_h40_mixed", 3, 1, 40, 700, 4096, extra_topk=200, extra_tokens_per_seq=1024), 16),
 ], ids=lambda x: x.name if isinstance(x, Spec) else str(x))
 def test_decode_64_head_extra_cache_long_parts(spec, per_part):
-    """Extra-cache decodes (two-half kernel) with long parts (12 and more sub-tiles), whose segments
-    start inside either cache's sub-tiles or cross from the one to the other."""
+    """Extra-cache decodes in the single-stream kernel (parts of 12 and more sub-tiles), whose
+    segments start inside either cache's sub-tiles or cross from the one to the other."""
     w = make_workload(spec, seed=43)
     out, lse, md = _decode(w, num_parts=_stream_parts(spec, per_part))
     ref_out, ref_lse = _oracle(w)
@@ -454,11 +453,14 @@ def test_64_head_ignored_runs_in_either_cache(per_part):
     (Spec("two_half_h64_spread", 2, 1, 64, 2048, 8192, values="spread", neg="tail10"), 2),
     (Spec("two_half_h16", 3, 1, 16, 700, 4096), 4),
     (Spec("two_half_h40_multi_segment", 3, 2, 40, 333, 2048, neg="frac5"), 3),
+    (Spec("two_half_h64_mixed", 2, 2, 64, 500, 4096, extra_topk=200, extra_tokens_per_seq=1024,
+          neg="frac5"), 4),
+    (Spec("two_half_h32_fp4_only", 3, 1, 32, 0, 64, extra_topk=300, extra_tokens_per_seq=1024), 2),
 ], ids=lambda x: x.name if isinstance(x, Spec) else str(x))
 def test_decode_two_half_kernel_short_parts(spec, per_part):
-    """fp8-only decodes whose parts average fewer than 6 sub-tiles, which run the two-half 64-head
-    kernel (mla_decode.hip) rather than the single-stream one."""
-    units = -(-spec.topk // 64)
+    """Decodes whose parts average fewer than 6 sub-tiles, which run the two-half 64-head kernel
+    (mla_decode.hip) rather than the single-stream one."""
+    units = -(-spec.topk // 64) + -(-spec.extra_topk // 64)
     parts = -(-2 * spec.rows * units // per_part)
     assert 2 * spec.rows * units < 6 * parts
     w = make_workload(spec, seed=47)

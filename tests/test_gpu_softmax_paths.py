@@ -160,6 +160,8 @@ def test_score_growth_reaches_the_rescale_paths(name, h_q, extra, mode):
             if mode == "extreme":
                 assert growth.max() > 64, f"{name} row {r}: growth {growth.max():.1f} <= 64"
     d = to_dev(w)
+    # h_q <= 64: one part per row (8 fp8 sub-tiles, and 4 fp4 ones with the extra cache) runs the
+    # single-stream kernel, three parts per row the two-half kernel
     md = mla.get_metadata(spec.batch, spec.seq_len_q, h_q, spec.topk, extra, num_parts=rows)
     out, lse = mla.sparse_decode(d["q"], d["k_cache"], d["indices"], w["softmax_scale"], md,
                                  d.get("extra_k_cache"), d.get("extra_indices"))
@@ -185,7 +187,7 @@ STREAM_CASES = [
 
 @pytest.mark.parametrize("name,h_q,mode", STREAM_CASES, ids=[c[0] for c in STREAM_CASES])
 def test_score_growth_single_stream_64_head_kernel(name, h_q, mode):
-    """The single-stream 64-head kernel (fp8 only, parts of at least 6 sub-tiles) takes
+    """The single-stream 64-head kernel (parts of at least 6 sub-tiles) takes
     probabilities against each head's first live sub-tile like the 128-head kernel: "extreme" rows
     grow by more than 64 log2 units past it, which forces the second pass."""
     spec = Spec(name, 4, 1, h_q, 1024, 8192)

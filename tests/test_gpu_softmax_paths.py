@@ -1,8 +1,9 @@
 """GPU parity on inputs built to reach the softmax's rarely taken paths.
 
-The 64-head kernel (h_q <= 64) keeps a running maximum per head and rescales its output accumulator
-only when a later sub-tile's maximum exceeds it by more than 8 (log2 units); the 128-head kernel
-takes probabilities against the first live sub-tile's maximum and computes a segment again when a
+The two-half 64-head kernel (h_q <= 64, short parts) keeps a running maximum per head and rescales
+its output accumulator only when a later sub-tile's maximum exceeds it by more than 8 (log2 units);
+the single-stream 64-head kernel (h_q <= 64, parts of 6 or more sub-tiles) and the 128-head kernel
+take probabilities against the first live sub-tile's maximum and compute a segment again when a
 later score exceeds that reference by more than 64. Random N(0,1) caches reach neither path, so
 these inputs control the scores:
 

@@ -118,25 +118,30 @@ def _controlled(spec, seed, mode):
 
 
 CASES = [
-    # (name, h_q, extra_topk, mode)
-    ("h16_fp8_moderate", 16, 0, "moderate"),
-    ("h64_fp8_moderate", 64, 0, "moderate"),
-    ("h16_fp4_moderate", 16, 96, "moderate"),
-    ("h64_fp4_moderate", 64, 96, "moderate"),
-    ("h128_fp8_moderate", 128, 0, "moderate"),
-    ("h128_fp4_moderate", 128, 96, "moderate"),
-    ("h16_fp8_extreme", 16, 0, "extreme"),
-    ("h64_fp8_extreme", 64, 0, "extreme"),
-    ("h64_fp4_extreme", 64, 96, "extreme"),
-    ("h128_fp8_extreme", 128, 0, "extreme"),
-    ("h128_fp4_extreme", 128, 96, "extreme"),
+    # (name, h_q, topk, extra_topk, mode)
+    ("h16_fp8_moderate", 16, 256, 0, "moderate"),
+    ("h64_fp8_moderate", 64, 256, 0, "moderate"),
+    ("h16_fp4_moderate", 16, 256, 96, "moderate"),
+    ("h64_fp4_moderate", 64, 256, 96, "moderate"),
+    ("h128_fp8_moderate", 128, 256, 0, "moderate"),
+    ("h128_fp4_moderate", 128, 256, 96, "moderate"),
+    ("h16_fp8_extreme", 16, 256, 0, "extreme"),
+    ("h64_fp8_extreme", 64, 256, 0, "extreme"),
+    ("h64_fp4_extreme", 64, 256, 96, "extreme"),
+    ("h128_fp8_extreme", 128, 256, 0, "extreme"),
+    ("h128_fp4_extreme", 128, 256, 96, "extreme"),
+    # rows of 2 fp8 and 2 fp4 sub-tiles: whole rows also run the two-half kernel, whose running
+    # maximum then grows inside the fp4 sub-tiles
+    ("h16_fp4_moderate_short", 16, 64, 64, "moderate"),
+    ("h64_fp4_moderate_short", 64, 64, 64, "moderate"),
+    ("h64_fp4_extreme_short", 64, 64, 64, "extreme"),
 ]
 
 
-@pytest.mark.parametrize("name,h_q,extra,mode", CASES, ids=[c[0] for c in CASES])
-def test_score_growth_reaches_the_rescale_paths(name, h_q, extra, mode):
+@pytest.mark.parametrize("name,h_q,topk,extra,mode", CASES, ids=[c[0] for c in CASES])
+def test_score_growth_reaches_the_rescale_paths(name, h_q, topk, extra, mode):
     # one query row per sequence, so that no two rows share (and rewrite) a token's record
-    spec = Spec(name, 4, 1, h_q, 256, 4096, extra_topk=extra,
+    spec = Spec(name, 4, 1, h_q, topk, 4096, extra_topk=extra,
                 extra_tokens_per_seq=1024 if extra else 0)
     w = _controlled(spec, seed=61 + h_q + extra, mode=mode)
     rows = spec.rows
@@ -161,8 +166,9 @@ def test_score_growth_reaches_the_rescale_paths(name, h_q, extra, mode):
             if mode == "extreme":
                 assert growth.max() > 64, f"{name} row {r}: growth {growth.max():.1f} <= 64"
     d = to_dev(w)
-    # h_q <= 64: one part per row (8 fp8 sub-tiles, and 4 fp4 ones with the extra cache) runs the
-    # single-stream kernel, three parts per row the two-half kernel
+    # h_q <= 64: one part per row of 8 fp8 sub-tiles (and 4 fp4 ones with the extra cache) runs
+    # the single-stream kernel, of 4 sub-tiles (the short rows) and three parts per row the
+    # two-half kernel
     md = mla.get_metadata(spec.batch, spec.seq_len_q, h_q, spec.topk, extra, num_parts=rows)
     out, lse = mla.sparse_decode(d["q"], d["k_cache"], d["indices"], w["softmax_scale"], md,
                                  d.get("extra_k_cache"), d.get("extra_indices"))

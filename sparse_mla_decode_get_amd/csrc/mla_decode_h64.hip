@@ -22,9 +22,11 @@
 //            the dequantization and the K operands of the next QK^T between them.
 // Gathers, index loads, the raw-record and bf16 tile layouts and the dequantization are those of
 // the 128-head kernel. With an extra cache (EXTRA) a segment's units past the row's fp8 units are
-// fp4 units; the choice is made per sub-tile with wave-uniform branches, and an fp4 sub-tile issues
-// the same five record copies as an fp8 one (two of them read the zero record into chunks the fp4
-// layout leaves unused), so the fixed s_waitcnt counts hold for any mix.
+// fp4 units. Phase A is compiled once per format of the sub-tile it dequantizes, chosen by a
+// wave-uniform branch per iteration; phase B branches per dequantization step instead (a copy of
+// phase B per format makes the compiler move the 128 O accumulators where the copies join). An fp4
+// sub-tile issues the same five record copies as an fp8 one (two of them read the zero record into
+// chunks the fp4 layout leaves unused), so the fixed s_waitcnt counts hold for any mix.
 
 #include <type_traits>
 
@@ -494,9 +496,9 @@ void sparse_decode_h64_kernel(DecodeParams p) {
         float fsc = 0.0f;
         // step k of 16: quarter k % 4 of the lane's 16-value block k / 4 (fp8: two steps convert,
         // one writes; fp4: four e2m1 values times the block's e4m3 scale per step, written at the end)
-        auto dequant_step = [&](int k) {
+        auto dequant_step = [&](auto fp4, int k) {
           const int cc = k >> 2, part = k & 3;
-          if (EXTRA && dx) {
+          if constexpr (decltype(fp4)::value) {
             const u32x4& r = (cc >> 1) ? fr1 : fr0;
             const uint32_t w = r[2 * (cc & 1) + (part >> 1)];
             if (part == 0) fsc = e4m3_to_f32(sc2 >> (8 * cc));
@@ -535,7 +537,9 @@ void sparse_decode_h64_kernel(DecodeParams p) {
         int gv = 0;
         uint64_t gdat = 0, gdat2 = 0;
 
-        // phase A: QK^T of sub-tile s+1, step i = token block i % 2 of k-step i / 2
+        // phase A: QK^T of sub-tile s+1, step i = token block i % 2 of k-step i / 2; one copy per
+        // format of s+2's dequantization
+        auto phase_a = [&](auto fp4) {
 #pragma unroll
         for (int i = 0; i < 32; ++i) {
           // The P^T operands written at the end of the previous iteration (its last six LDS
@@ -555,7 +559,7 @@ void sparse_decode_h64_kernel(DecodeParams p) {
           if (i < 2) mfma_qk16_first(sacc[i], kb[i % kRing], qreg[0]);
           else mfma_qk16(sacc[i & 1], kb[i % kRing], qreg[i >> 1]);
           if (i == 1) {
-            if (EXTRA && dx) {
+            if constexpr (decltype(fp4)::value) {
               const uint32_t draw4 = raw_r4 + r2 * kRawBytes;
               sc2 = *reinterpret_cast<const __attribute__((address_space(3))) uint32_t*>(
                   (uintptr_t)(raw_s4 + r2 * kRawBytes));
@@ -609,9 +613,12 @@ void sparse_decode_h64_kernel(DecodeParams p) {
           }
           if (i == 10) rr0 = *(lds_u32x4_r*)(uintptr_t)(draw + 1024);
           if (i == 14) rr1 = *(lds_u32x4_r*)(uintptr_t)(draw + 1536);
-          if (i >= 8 && i < 16) dequant_step(i - 8);
+          if (i >= 8 && i < 16) dequant_step(fp4, i - 8);
           __builtin_amdgcn_sched_barrier(0);
         }
+        };
+        if (EXTRA && dx) phase_a(std::true_type{});
+        else phase_a(std::false_type{});
 
         // phase B: PV of sub-tile s. Step i accumulates block 2 b + hb (dim block 4w + b, head
         // block hb) over token half ks = i / 8 with V^T operand i / 2 and P^T operand (hb, ks).
@@ -680,7 +687,11 @@ void sparse_decode_h64_kernel(DecodeParams p) {
               pw[k] = __builtin_bit_cast(uint32_t, v2);
             }
           }
-          if (i >= 1 && i < 9) dequant_step(i + 7);
+          if (i >= 1 && i < 9) {
+            // per step: see the note on phase B at the top of the file
+            if (EXTRA && dx) dequant_step(std::true_type{}, i + 7);
+            else dequant_step(std::false_type{}, i + 7);
+          }
           if (i == 11) {
             // Start of iteration s+1: every V and P^T read of this iteration is complete,
             // idx(s+5) and the gather of s+3 have landed and the dequantization of s+2 is written.

@@ -17,15 +17,15 @@
 //
 // Iteration s of the pipeline, behind two workgroup barriers:
 //   phase A  the 32 QK^T MFMAs of sub-tile s+1 (16x16x32, two token blocks alternating), with the
-//            index load of s+6, the gather of s+4 and half the dequantization of s+2 between them;
-//   phase B  the 16 PV MFMAs of sub-tile s (32x32x16), with the softmax of s+1, the other half of
-//            the dequantization and the K operands of the next QK^T between them.
+//            index load of s+6, the gather of s+4 and the dequantization of s+2 between them;
+//   phase B  the 16 PV MFMAs of sub-tile s (32x32x16), with the softmax of s+1 and the K operands
+//            of the next QK^T between them.
 // Gathers, index loads, the raw-record and bf16 tile layouts and the dequantization are those of
 // the 128-head kernel. With an extra cache (EXTRA) a segment's units past the row's fp8 units are
-// fp4 units. Phase A is compiled once per format of the sub-tile it dequantizes, chosen by a
-// wave-uniform branch per iteration; phase B branches per dequantization step instead (a copy of
-// phase B per format makes the compiler move the 128 O accumulators where the copies join). An fp4
-// sub-tile issues the same five record copies as an fp8 one (two of them read the zero record into
+// fp4 units. Phase A, which holds all of the dequantization, is compiled once per format of the
+// sub-tile it dequantizes, chosen by one wave-uniform branch per iteration (with one wave per SIMD a
+// taken branch stalls the SIMD, so a branch per step costs; a copy of phase B per format would make
+// the compiler move the 128 O accumulators where the copies join). An fp4 sub-tile issues the same five record copies as an fp8 one (two of them read the zero record into
 // chunks the fp4 layout leaves unused), so the fixed s_waitcnt counts hold for any mix.
 
 #include <type_traits>
@@ -613,7 +613,8 @@ void sparse_decode_h64_kernel(DecodeParams p) {
           }
           if (i == 10) rr0 = *(lds_u32x4_r*)(uintptr_t)(draw + 1024);
           if (i == 14) rr1 = *(lds_u32x4_r*)(uintptr_t)(draw + 1536);
-          if (i >= 8 && i < 16) dequant_step(fp4, i - 8);
+          // dequantization of s+2, steps 8 .. 23 (chunks 2 and 3 of fp8 were read at steps 10, 14)
+          if (i >= 8 && i < 24) dequant_step(fp4, i - 8);
           __builtin_amdgcn_sched_barrier(0);
         }
         };
@@ -686,11 +687,6 @@ void sparse_decode_h64_kernel(DecodeParams p) {
               v2[1] = (__bf16)e[2 * k + 1];
               pw[k] = __builtin_bit_cast(uint32_t, v2);
             }
-          }
-          if (i >= 1 && i < 9) {
-            // per step: see the note on phase B at the top of the file
-            if (EXTRA && dx) dequant_step(std::true_type{}, i + 7);
-            else dequant_step(std::false_type{}, i + 7);
           }
           if (i == 11) {
             // Start of iteration s+1: every V and P^T read of this iteration is complete,

@@ -25,13 +25,16 @@ int tiles_per_row(int topk, int extra_topk, int* tiles_k) {
 //  - mla_decode_h64.hip: one software-pipelined sub-tile stream, one wave per SIMD; about 1.1 us
 //    per 32-token fp8 sub-tile, but a longer start than the other;
 //  - mla_decode.hip: two halves of four waves with a one-deep pipeline; about 1.6 us per sub-tile.
-// The first is taken when the parts average at least kStreamMinSubtiles sub-tiles of either cache
-// (measured on MI355X over 32 rows of 64 heads: 3 us ahead at 8 sub-tiles per part, level at 4,
-// behind at 2; with an fp4 cache of a fifth of the tokens, level at 20 and 5% ahead at 40).
+// The first is taken when the parts average at least kStreamMinSubtiles sub-tiles (measured on
+// MI355X over 32 rows of 64 heads: 3 us ahead at 8 sub-tiles per part, level at 4, behind at 2),
+// or kStreamMinSubtilesExtra with an fp4 cache of a fifth of the tokens (32 and 64 such rows: 3 us
+// behind at 6 sub-tiles per part, level or 3 us ahead at 8, 9% ahead at 80).
 bool wide_for(int h_q) { return h_q > 64; }
 constexpr int kStreamMinSubtiles = 6;
-bool h64_stream_for(int rows, int tiles, int parts) {
-  return 2 * (int64_t)rows * tiles >= (int64_t)kStreamMinSubtiles * parts;
+constexpr int kStreamMinSubtilesExtra = 8;
+bool h64_stream_for(int rows, int tiles, int parts, int extra_topk) {
+  const int64_t need = extra_topk > 0 ? kStreamMinSubtilesExtra : kStreamMinSubtiles;
+  return 2 * (int64_t)rows * tiles >= need * parts;
 }
 int group_heads(int h_q) { return wide_for(h_q) ? 128 : 64; }
 int head_groups(int h_q) { return (h_q + group_heads(h_q) - 1) / group_heads(h_q); }
@@ -199,7 +202,7 @@ int sparse_decode(const DecodeCall& c, const WorkspaceSource& ws) {
   hipStream_t s = (hipStream_t)c.stream;
   const int launched =
       wide_for(h_q) ? launch_sparse_decode_wide(p, parts, head_groups(h_q), s)
-      : h64_stream_for(rows, tiles, parts) ? launch_sparse_decode_h64(p, parts, head_groups(h_q), s)
+      : h64_stream_for(rows, tiles, parts, extra_topk) ? launch_sparse_decode_h64(p, parts, head_groups(h_q), s)
                                                        : launch_sparse_decode(p, parts, head_groups(h_q), 4, s);
   if (launched != 0) return MLA_ERR_HIP;
   if (split && c.fused) {

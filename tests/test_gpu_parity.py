@@ -356,15 +356,17 @@ def test_decode_replays_from_a_captured_graph(h_q):
 
 
 # ------------------------------------------------ the single-stream 64-head kernel (mla_decode_h64)
-# h_q <= 64 runs in that kernel when the parts average at least 6 sub-tiles of 32 tokens of either
-# cache (2 * rows * units / parts >= 6), as the default schedules of the larger shapes do; the cases
-# below are sized for it. Parts of fewer sub-tiles run the two-half kernel (mla_decode.hip).
+# h_q <= 64 runs in that kernel when the parts average at least 6 sub-tiles of 32 tokens
+# (2 * rows * units / parts >= 6), or 8 with an extra cache (units of both caches), as the default
+# schedules of the larger shapes do; the cases below are sized for it. Parts of fewer sub-tiles run
+# the two-half kernel (mla_decode.hip).
 
 def _stream_parts(spec, per_part):
-    """A part count that gives `per_part` sub-tiles per part (at least 6), units of both caches."""
+    """A part count that gives `per_part` sub-tiles per part (at least 6, or 8 with an extra cache),
+    units of both caches."""
     units = -(-spec.topk // 64) + -(-spec.extra_topk // 64)
     parts = max(1, 2 * spec.rows * units // per_part)
-    assert 2 * spec.rows * units >= 6 * parts
+    assert 2 * spec.rows * units >= (8 if spec.extra_topk else 6) * parts
     return parts
 
 
